@@ -1,0 +1,306 @@
+"""Python binding of libisd.so, the MI355X (gfx950) ISD step library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libisd.so; torch is used for device memory and the current stream. The
+names mirror the C ABI in include/isd.h. There is no fallback: if the
+library is missing, importing works but every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libisd.so")
+
+ISD_BF16 = 1
+ISD_F32 = 2
+PAGE_SIZE = 16
+
+DEV_PAGE_OOB = 1
+DEV_CAPACITY = 2
+DEV_NONFINITE = 4
+DEV_TOKEN_OOB = 8
+DEV_STATE = 16
+
+_DTYPES = {torch.bfloat16: ISD_BF16, torch.float32: ISD_F32}
+
+
+class IsdError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+# ------------------------------------------------------------------ C types
+class IsdKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("table_stride", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class IsdSeqState(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("n_draft", "drafts", "q_x", "q_m", "q_s", "q_row")]
+
+
+class IsdAcceptArgs(ctypes.Structure):
+    _fields_ = [
+        ("C", ctypes.c_int32), ("N", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("rows", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("logits", ctypes.c_void_p), ("prev_logits", ctypes.c_void_p),
+        ("ld", ctypes.c_int64),
+        ("in_", IsdSeqState), ("out", IsdSeqState),
+        ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64),
+        ("accepted", ctypes.c_void_p), ("n_emit", ctypes.c_void_p),
+        ("emit", ctypes.c_void_p), ("kv_commit", ctypes.c_void_p),
+        ("p_x", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p),
+        ("row_m", ctypes.c_void_p), ("row_s", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("dev_err", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+_SIGNATURES = {
+    "isd_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "isd_version": (ctypes.c_int, []),
+    "isd_kv_write": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "isd_attention_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.POINTER(IsdKvCache), ctypes.c_int, ctypes.c_int]),
+    "isd_attention": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_void_p]),
+    "isd_accept_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "isd_accept": (ctypes.c_int, [ctypes.POINTER(IsdAcceptArgs), ctypes.c_void_p]),
+    "isd_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "isd_lora_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int]),
+    "gated_lora_apply": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "isd_linear_gated": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded library; raises if libisd.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python draft_verify_decoding_amd/build.py (no CPU fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code):
+    return lib().isd_strerror(int(code)).decode()
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise IsdError(rc, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+# ------------------------------------------------------------------ KV cache
+class KVCache:
+    """Device page pools in the library's layout plus a block table.
+
+    k_pages/v_pages hold num_pages * Hkv * D * 16 elements each; the layout
+    of a page is documented in include/isd.h.
+    """
+
+    def __init__(self, num_pages, num_kv_heads, head_dim, dtype, block_table, device="cuda"):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.dtype = dtype
+        n = num_pages * num_kv_heads * head_dim * PAGE_SIZE
+        self.k_pages = torch.zeros(n, dtype=dtype, device=device)
+        self.v_pages = torch.zeros(n, dtype=dtype, device=device)
+        self.block_table = block_table.to(device=device, dtype=torch.int32).contiguous()
+
+    def c_struct(self):
+        return IsdKvCache(
+            self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.block_table.data_ptr(),
+            self.block_table.shape[1], self.num_pages, PAGE_SIZE, self.num_kv_heads,
+            self.head_dim, _DTYPES[self.dtype])
+
+
+def isd_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
+    """Write k, v [C, rows, Hkv, D] at positions pos0[b] + r (r < nrows[b])."""
+    C, rows = k.shape[0], k.shape[1]
+    s = kv.c_struct()
+    rc = lib().isd_kv_write(ctypes.byref(s), _p(k), _p(v), _p(pos0), _p(nrows), C, rows,
+                            _p(dev_err), _stream(stream))
+    _check(rc, "isd_kv_write")
+
+
+def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, chunk=0):
+    s = kv.c_struct()
+    return int(lib().isd_attention_workspace_size(C, rows, num_q_heads, ctypes.byref(s), max_len, chunk))
+
+
+def isd_attention(kv, q, ctx, max_len, scale=None, chunk=0, out=None, ws=None, dev_err=None, stream=None):
+    """out [C, rows, Hq, D] fp32 = causal attention of q over the pages."""
+    C, rows, Hq, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((C, rows, Hq, D), dtype=torch.float32, device=q.device)
+    need = isd_attention_workspace_size(kv, C, rows, Hq, max_len, chunk)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    s = kv.c_struct()
+    rc = lib().isd_attention(ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
+                             int(chunk), _p(out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                             _p(dev_err), _stream(stream))
+    _check(rc, "isd_attention")
+    return out
+
+
+# -------------------------------------------------------------------- accept
+class SeqState:
+    """Per-sequence decoding state on the device (see isd_seq_state)."""
+
+    def __init__(self, C, N, device="cuda"):
+        nd = N - 1
+        self.C, self.N = C, N
+        self.n_draft = torch.zeros(C, dtype=torch.int32, device=device)
+        self.drafts = torch.full((C, nd), -1, dtype=torch.int32, device=device)
+        self.q_x = torch.zeros((C, nd), dtype=torch.float32, device=device)
+        self.q_m = torch.zeros((C, nd), dtype=torch.float32, device=device)
+        self.q_s = torch.zeros((C, nd), dtype=torch.float32, device=device)
+        self.q_row = torch.zeros(C, dtype=torch.int32, device=device)
+
+    def c_struct(self):
+        return IsdSeqState(*(t.data_ptr() for t in
+                             (self.n_draft, self.drafts, self.q_x, self.q_m, self.q_s, self.q_row)))
+
+    def copy_(self, other):
+        for name in ("n_draft", "drafts", "q_x", "q_m", "q_s", "q_row"):
+            getattr(self, name).copy_(getattr(other, name))
+        return self
+
+
+def isd_accept_workspace_size(C, N, V, rows):
+    return int(lib().isd_accept_workspace_size(C, N, V, rows))
+
+
+class AcceptOutputs:
+    def __init__(self, C, N, rows, device, diag):
+        self.accepted = torch.empty(C, dtype=torch.int32, device=device)
+        self.n_emit = torch.empty(C, dtype=torch.int32, device=device)
+        self.emit = torch.empty((C, N), dtype=torch.int32, device=device)
+        self.kv_commit = torch.empty(C, dtype=torch.int32, device=device)
+        self.p_x = self.resid_mass = self.row_m = self.row_s = None
+        if diag:
+            self.p_x = torch.empty((C, N - 1), dtype=torch.float32, device=device)
+            self.resid_mass = torch.empty(C, dtype=torch.float32, device=device)
+            self.row_m = torch.empty((C, rows), dtype=torch.float32, device=device)
+            self.row_s = torch.empty((C, rows), dtype=torch.float32, device=device)
+
+
+def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
+               diag=False, dev_err=None, stream=None):
+    """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
+    AcceptOutputs (device tensors) and writes state_out."""
+    C, rows, ld = logits.shape
+    V = ld if V is None else V
+    if out is None:
+        out = AcceptOutputs(C, N, rows, logits.device, diag)
+    need = isd_accept_workspace_size(C, N, V, rows)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    args = IsdAcceptArgs()
+    args.C, args.N, args.V, args.rows = C, N, V, rows
+    args.dtype = _dtype_code(logits)
+    args.logits = logits.data_ptr()
+    args.prev_logits = None if prev_logits is None else prev_logits.data_ptr()
+    args.ld = ld
+    args.in_ = state_in.c_struct()
+    args.out = state_out.c_struct()
+    args.seed, args.step = int(seed), int(step)
+    args.accepted, args.n_emit = out.accepted.data_ptr(), out.n_emit.data_ptr()
+    args.emit, args.kv_commit = out.emit.data_ptr(), out.kv_commit.data_ptr()
+    for name in ("p_x", "resid_mass", "row_m", "row_s"):
+        t = getattr(out, name)
+        setattr(args, name, None if t is None else t.data_ptr())
+    args.ws = ws.data_ptr()
+    args.ws_bytes = ws.numel() * ws.element_size()
+    args.dev_err = None if dev_err is None else dev_err.data_ptr()
+    _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
+    return out
+
+
+# --------------------------------------------------------------- projections
+def isd_linear(x, W, y=None, stream=None):
+    M, K = x.shape
+    Nout = W.shape[0]
+    if y is None:
+        y = torch.empty((M, Nout), dtype=torch.float32, device=x.device)
+    _check(lib().isd_linear(_p(x), _p(W), M, K, Nout, _p(y), _stream(stream)), "isd_linear")
+    return y
+
+
+def isd_lora_workspace_size(M, r):
+    return int(lib().isd_lora_workspace_size(M, r))
+
+
+def gated_lora_apply(x, A, B, is_mask, y, scale=1.0, ws=None, stream=None):
+    M, K = x.shape
+    r, Nout = A.shape[0], B.shape[0]
+    if ws is None:
+        ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
+    rc = lib().gated_lora_apply(_p(x), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
+                                _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "gated_lora_apply")
+    return y
+
+
+def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=None):
+    M, K = x.shape
+    r, Nout = A.shape[0], W.shape[0]
+    if y is None:
+        y = torch.empty((M, Nout), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
+    rc = lib().isd_linear_gated(_p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
+                                _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "isd_linear_gated")
+    return y

@@ -1,0 +1,610 @@
+// The accept side of one ISD step on gfx950: vocab softmax statistics, the
+// min(1, p/q) test, the residual or bonus draw and the next drafts.
+//
+// What the step computes is fixed by the I-DLM page (fr.news.hada.io,
+// "Documentation et ressources > Inference & ISD": proposals q at MASK
+// positions, verification p at clean positions, keep a draft with
+// probability min(1, p(x)/q(x)), which keeps the AR distribution). The
+// residual draw normalize(max(0, p - q)) after the first rejection is the
+// standard rejection-sampling step behind that guarantee; the bonus draw and
+// the FULL/FRESH alternation are what reproduce the page's tokens-per-forward
+// closed form ("Speedup Factor Explorer").
+//
+// Three launches, all HBM-streaming and deterministic:
+//   stats   one pass over every logits row the step may read: per 8192-entry
+//           chunk, the max and sum of exp(l - max) (fp32 from exact bf16).
+//   sample  grid (slices, sequences). Every workgroup rebuilds the row
+//           statistics and the accept decision from the chunk stats (same
+//           fixed-order arithmetic, so all agree). On a rejection each slice
+//           sums the residual max(0, P_a - Q_{a+1}) over its chunk; when all
+//           drafts pass, slice k rescans the one chunk where the CDF of row
+//           n + k crosses its uniform (bonus for k = 0, proposals after).
+//   finish  one workgroup per sequence: residual chunk choice and rescan,
+//           outputs, next state.
+#include "isd_common.hpp"
+
+namespace isd {
+
+constexpr int kChunk = 8192;     // vocab entries per stats chunk
+constexpr int kThreads = 256;    // threads per workgroup
+constexpr int kPerThread = 32;   // entries per thread in a chunk
+constexpr int kMaxN = 8;
+static_assert(kThreads * kPerThread == kChunk, "chunk tiling");
+
+struct AcceptParams {
+  const void* logits;
+  const void* prev_logits;
+  long ld;
+  int C, N, V, rows, nch, ns;
+  isd_seq_state in, out;
+  uint64_t seed, step;
+  int32_t *accepted, *n_emit, *emit, *kv_commit;
+  float *p_x, *resid_mass, *row_m, *row_s;
+  float2* stats;    // [C][rows][nch] (chunk max, chunk sum)
+  float* resid;     // [C][ns] residual slice sums
+  int2* samp;       // [C][N] (token, bits of q(x)) from the sample kernel
+  int32_t* dev_err;
+};
+
+// ------------------------------------------------------------ Philox4x64-10
+// Salmon et al., SC'11: two 64x64->128 multiplies per round, Weyl key bumps,
+// ten rounds. Counter (slot, b, step, 0), key (seed, 0).
+__device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                                 uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+__device__ __forceinline__ float uniform_of(uint64_t w0) {
+  return (static_cast<float>(static_cast<uint32_t>(w0 >> 41)) + 0.5f) * 0x1p-23f;
+}
+
+// -------------------------------------------------------------- arithmetic
+// Unnormalised softmax weight relative to the row max M (as exp2 of a
+// log2-scaled argument). Every place that needs P(x) uses these helpers so
+// that equal inputs give equal bits.
+__device__ __forceinline__ float weight_of(float l, float m_log2) { return fast_exp2(fmaf(l, kLog2e, -m_log2)); }
+__device__ __forceinline__ float prob_of(float l, float M, float S) { return weight_of(l, M * kLog2e) / S; }
+
+// Merge two (max, sum exp(l - max)) pairs.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) {
+    m = mm;
+    s = 0.f;
+    return;
+  }
+  s = s * fast_exp2((m - mm) * kLog2e) + s2 * fast_exp2((m2 - mm) * kLog2e);
+  m = mm;
+}
+
+template <typename E>
+__device__ __forceinline__ const E* row_ptr(const void* base, long ld, int rows, int b, int r) {
+  return static_cast<const E*>(base) + (static_cast<long>(b) * rows + r) * ld;
+}
+
+template <typename E>
+__device__ __forceinline__ float load_elem(const E* row, int v) {
+  return Elem<E>::to_f32(row[v]);
+}
+
+// Load this thread's 32 entries of chunk c (entries >= V become -inf).
+template <typename E>
+__device__ __forceinline__ void load_chunk_slice(const E* row, int V, int c, float (&x)[kPerThread]) {
+  constexpr int KP = Elem<E>::kPerVec;
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+#pragma unroll
+  for (int q = 0; q < kPerThread / KP; ++q) {
+    const int vq = v0 + q * KP;
+    if (vq + KP <= V) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + vq);
+      float f[KP];
+      unpack16(w, f);
+#pragma unroll
+      for (int k = 0; k < KP; ++k) x[q * KP + k] = f[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) x[q * KP + k] = (vq + k < V) ? load_elem(row, vq + k) : -INFINITY;
+    }
+  }
+}
+
+// Workgroup reduction of (max, sum) pairs in a fixed tree.
+__device__ __forceinline__ void block_reduce_ms(float& m, float& s) {
+  __shared__ float sm[kThreads / kWave], ss[kThreads / kWave];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) merge_ms(m, s, __shfl_xor(m, off, kWave), __shfl_xor(s, off, kWave));
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) {
+    sm[w] = m;
+    ss[w] = s;
+  }
+  __syncthreads();
+  m = sm[0];
+  s = ss[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) merge_ms(m, s, sm[i], ss[i]);
+  __syncthreads();
+}
+
+__device__ __forceinline__ float block_sum(float v) {
+  __shared__ float sv[kThreads / kWave];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  if ((threadIdx.x % kWave) == 0) sv[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float t = sv[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) t += sv[i];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix over threads (thread order) of v; returns the prefix.
+__device__ __forceinline__ float block_exclusive_scan(float v) {
+  __shared__ float sw[kThreads / kWave];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  float inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  float excl = __shfl_up(inc, 1, kWave);
+  if (lane == 0) excl = 0.f;
+  if (lane == kWave - 1) sw[w] = inc;
+  __syncthreads();
+  float base = 0.f;
+  for (int i = 0; i < w; ++i) base += sw[i];
+  __syncthreads();
+  return base + excl;
+}
+
+// ============================================================ stats kernel
+template <typename E>
+__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  int n = p.in.n_draft[b];
+  n = n < 0 ? 0 : (n > p.N - 1 ? p.N - 1 : n);
+  if (r > n + p.N - 1) return;
+  float x[kPerThread];
+  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
+  float s = 0.f;
+  if (m != -INFINITY) {
+    const float ml = m * kLog2e;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) s += weight_of(x[k], ml);
+  }
+  block_reduce_ms(m, s);
+  if (threadIdx.x == 0) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c] = make_float2(m, s);
+}
+
+// ------------------------------------------------ shared per-sequence logic
+struct Decision {
+  int n, a, err;        // err: ISD_DEV_* bits, 0 if the step can be taken
+  float M[2 * kMaxN];   // row max
+  float S[2 * kMaxN];   // row sum exp(l - M)
+  float u[2 * kMaxN];   // uniforms by slot
+  float px[kMaxN];      // P_{j-1}(x_j) of tested drafts
+};
+
+// Rebuild row statistics, uniforms and the accept decision of sequence b.
+// Every workgroup that calls this computes the same values. Result in LDS.
+template <typename E>
+__device__ void decide(const AcceptParams& p, int b, Decision& d) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int n = p.in.n_draft[b];
+    int err = 0;
+    if (n < 0 || n > p.N - 1) {
+      err |= ISD_DEV_STATE;
+      n = 0;
+    }
+    if (n > 0 && (!p.prev_logits || p.in.q_row[b] < 0 || p.in.q_row[b] + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
+    for (int j = 0; j < n; ++j) {
+      const int x = p.in.drafts[b * (p.N - 1) + j];
+      if (x < 0 || x >= p.V) err |= ISD_DEV_TOKEN_OOB;
+    }
+    d.n = n;
+    d.err = err;
+  }
+  __syncthreads();
+  const int n = d.n;
+  const int nrows = n + p.N;  // rows 0 .. n + N - 1
+  if (tid < nrows) {
+    const float2* st = p.stats + (static_cast<long>(b) * p.rows + tid) * p.nch;
+    float M = -INFINITY;
+    for (int c = 0; c < p.nch; ++c) M = fmaxf(M, st[c].x);
+    float S = 0.f;
+    if (M != -INFINITY) {
+      for (int c = 0; c < p.nch; ++c) S += st[c].y * fast_exp2((st[c].x - M) * kLog2e);
+    }
+    d.M[tid] = M;
+    d.S[tid] = S;
+    if (!(M > -INFINITY && M < INFINITY && S > 0.f && S < INFINITY)) atomicOr(&d.err, static_cast<int>(ISD_DEV_NONFINITE));
+  }
+  if (tid < 2 * p.N)
+    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), p.step, 0ull, p.seed, 0ull));
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0;
+    for (int j = 0; j < kMaxN; ++j) d.px[j] = NAN;
+    if (!d.err) {
+      for (int j = 1; j <= n; ++j) {
+        const int x = p.in.drafts[b * (p.N - 1) + j - 1];
+        const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, j - 1), x);
+        const float px = prob_of(l, d.M[j - 1], d.S[j - 1]);
+        const float qx = p.in.q_x[b * (p.N - 1) + j - 1];
+        d.px[j - 1] = px;
+        // u * q < p compared exactly (fp32 operands, exact fp64 product).
+        if (static_cast<double>(d.u[j]) * static_cast<double>(qx) < static_cast<double>(px))
+          ++a;
+        else
+          break;
+      }
+    }
+    d.a = a;
+  }
+  __syncthreads();
+}
+
+// Residual weight max(0, P_a(v) - Q(v)) of one entry.
+// Both products are rounded before the subtraction (no fused multiply-add),
+// so equal P and Q cancel exactly.
+__device__ __forceinline__ float resid_weight(float l, float lq, float ma_l2, float inv_sa, float mq_l2, float inv_sq) {
+#pragma clang fp contract(off)
+  const float pa = weight_of(l, ma_l2) * inv_sa;
+  const float qa = weight_of(lq, mq_l2) * inv_sq;
+  return fmaxf(0.f, pa - qa);
+}
+
+// Inverse-CDF search inside one chunk: weights w[] of this thread's 32
+// entries (thread order = token order), target t_rel measured from the start
+// of the chunk. Returns the smallest crossing token id, or the last token
+// with non-zero weight in the chunk when rounding leaves no crossing.
+__device__ int chunk_search(const float (&w)[kPerThread], int c, float t_rel) {
+  __shared__ int s_tok, s_last;
+  if (threadIdx.x == 0) {
+    s_tok = 0x7fffffff;
+    s_last = -1;
+  }
+  float local = 0.f;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) local += w[k];
+  const float base = block_exclusive_scan(local);  // also syncs
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  const float tr = t_rel - base;
+  if (tr >= 0.f && local > tr) {
+    float acc = 0.f;
+    int hit = -1;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      acc += w[k];
+      if (hit < 0 && acc > tr) hit = v0 + k;
+    }
+    if (hit >= 0) atomicMin(&s_tok, hit);
+  }
+  int last = -1;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k)
+    if (w[k] > 0.f) last = v0 + k;
+  if (last >= 0) atomicMax(&s_last, last);
+  __syncthreads();
+  const int tok = s_tok != 0x7fffffff ? s_tok : s_last;
+  __syncthreads();
+  return tok;
+}
+
+// Choose the chunk of a row whose (rescaled) chunk sums cross u * S.
+// Returns the chunk and writes the target relative to its start.
+__device__ __forceinline__ int pick_chunk_from_stats(const float2* st, int nch, float M, float t, float* t_rel) {
+  float run = 0.f;
+  int last_nz = 0;
+  for (int c = 0; c < nch; ++c) {
+    const float wc = st[c].y * fast_exp2((st[c].x - M) * kLog2e);
+    if (wc > 0.f) last_nz = c;
+    if (run + wc > t) {
+      *t_rel = t - run;
+      return c;
+    }
+    run += wc;
+  }
+  *t_rel = INFINITY;  // rounding: take the last non-zero token of that chunk
+  return last_nz;
+}
+
+// Sample from softmax(row r) with uniform u: returns the token.
+template <typename E>
+__device__ int sample_row(const AcceptParams& p, int b, int r, float M, float S, float u) {
+  const float2* st = p.stats + (static_cast<long>(b) * p.rows + r) * p.nch;
+  float t_rel;
+  const int c = pick_chunk_from_stats(st, p.nch, M, u * S, &t_rel);
+  float x[kPerThread];
+  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
+  const float ml = M * kLog2e;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) x[k] = weight_of(x[k], ml);
+  return chunk_search(x, c, t_rel);
+}
+
+// Residual weights of this thread's slice of chunk c.
+template <typename E>
+__device__ __forceinline__ void resid_slice(const AcceptParams& p, int b, const Decision& d, int c,
+                                            float (&w)[kPerThread]) {
+  const int a = d.a;
+  float x[kPerThread], y[kPerThread];
+  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, a), p.V, c, x);
+  const int qrow = p.in.q_row[b] + a;
+  load_chunk_slice<E>(row_ptr<E>(p.prev_logits, p.ld, p.rows, b, qrow), p.V, c, y);
+  const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
+  const float mq_l2 = p.in.q_m[b * (p.N - 1) + a] * kLog2e, inv_sq = 1.f / p.in.q_s[b * (p.N - 1) + a];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) w[k] = (x[k] == -INFINITY) ? 0.f : resid_weight(x[k], y[k], ma_l2, inv_sa, mq_l2, inv_sq);
+}
+
+// =========================================================== sample kernel
+template <typename E>
+__global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p) {
+  const int slice = blockIdx.x, b = blockIdx.y;
+  __shared__ Decision d;
+  decide<E>(p, b, d);
+  if (d.err) return;
+  const int n = d.n, a = d.a;
+  if (a < n) {
+    if (slice >= p.nch) return;
+    float w[kPerThread];
+    resid_slice<E>(p, b, d, slice, w);
+    float local = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) local += w[k];
+    const float tot = block_sum(local);
+    if (threadIdx.x == 0) p.resid[static_cast<long>(b) * p.ns + slice] = tot;
+  } else {
+    if (slice >= p.N) return;
+    const int r = n + slice;  // slice 0: bonus row n; slice k: proposal row n + k
+    const int tok = sample_row<E>(p, b, r, d.M[r], d.S[r], d.u[p.N + slice]);
+    if (threadIdx.x == 0) {
+      const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
+      p.samp[b * p.N + slice] = make_int2(tok, __float_as_int(prob_of(l, d.M[r], d.S[r])));
+    }
+  }
+}
+
+// =========================================================== finish kernel
+template <typename E>
+__global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p) {
+  const int b = blockIdx.x;
+  const int N = p.N, nd = N - 1;
+  __shared__ Decision d;
+  decide<E>(p, b, d);
+  const int tid = threadIdx.x;
+  if (d.err) {
+    if (tid == 0) {
+      p.accepted[b] = -1;
+      p.n_emit[b] = 0;
+      p.kv_commit[b] = 0;
+      for (int k = 0; k < N; ++k) p.emit[b * N + k] = -1;
+      p.out.n_draft[b] = p.in.n_draft[b];
+      p.out.q_row[b] = p.in.q_row[b];
+      for (int k = 0; k < nd; ++k) {
+        p.out.drafts[b * nd + k] = p.in.drafts[b * nd + k];
+        p.out.q_x[b * nd + k] = p.in.q_x[b * nd + k];
+        p.out.q_m[b * nd + k] = p.in.q_m[b * nd + k];
+        p.out.q_s[b * nd + k] = p.in.q_s[b * nd + k];
+      }
+      if (p.resid_mass) p.resid_mass[b] = -1.f;
+      if (p.p_x)
+        for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = NAN;
+      if (p.row_m)
+        for (int r = 0; r < p.rows; ++r) {
+          p.row_m[b * p.rows + r] = NAN;
+          p.row_s[b * p.rows + r] = NAN;
+        }
+      set_dev_err(p.dev_err, static_cast<uint32_t>(d.err));
+    }
+    return;
+  }
+  const int n = d.n, a = d.a;
+  __shared__ int s_t;
+  __shared__ float s_mass;
+  if (a < n) {
+    // Residual: pick the chunk from the slice sums, rescan it.
+    if (tid == 0) {
+      float W = 0.f;
+      for (int c = 0; c < p.nch; ++c) W += p.resid[static_cast<long>(b) * p.ns + c];
+      s_mass = W;
+    }
+    __syncthreads();
+    const float W = s_mass;
+    int tok;
+    if (W > 0.f) {
+      const float t = d.u[N] * W;
+      __shared__ int s_c;
+      __shared__ float s_trel;
+      if (tid == 0) {
+        float run = 0.f;
+        int c_sel = -1, last_nz = 0;
+        float trel = INFINITY;
+        for (int c = 0; c < p.nch; ++c) {
+          const float wc = p.resid[static_cast<long>(b) * p.ns + c];
+          if (wc > 0.f) last_nz = c;
+          if (c_sel < 0 && run + wc > t) {
+            c_sel = c;
+            trel = t - run;
+          }
+          run += wc;
+        }
+        s_c = c_sel >= 0 ? c_sel : last_nz;
+        s_trel = c_sel >= 0 ? trel : INFINITY;
+      }
+      __syncthreads();
+      float w[kPerThread];
+      resid_slice<E>(p, b, d, s_c, w);
+      tok = chunk_search(w, s_c, s_trel);
+    } else {
+      // No residual mass left (P_a <= Q_{a+1} everywhere): draw from P_a.
+      tok = sample_row<E>(p, b, a, d.M[a], d.S[a], d.u[N]);
+    }
+    if (tid == 0) s_t = tok;
+  } else {
+    if (tid == 0) s_t = p.samp[b * N].x;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int t = s_t;
+    p.accepted[b] = a;
+    p.n_emit[b] = a + 1;
+    p.kv_commit[b] = a + 1;
+    for (int k = 0; k < N; ++k) {
+      int v = -1;
+      if (k < a) v = p.in.drafts[b * nd + k];
+      if (k == a) v = t;
+      p.emit[b * N + k] = v;
+    }
+    if (a == n) {
+      p.out.n_draft[b] = nd;
+      p.out.q_row[b] = n + 1;
+      for (int k = 1; k <= nd; ++k) {
+        const int2 sp = p.samp[b * N + k];
+        p.out.drafts[b * nd + k - 1] = sp.x;
+        p.out.q_x[b * nd + k - 1] = __int_as_float(sp.y);
+        p.out.q_m[b * nd + k - 1] = d.M[n + k];
+        p.out.q_s[b * nd + k - 1] = d.S[n + k];
+      }
+    } else {
+      p.out.n_draft[b] = 0;
+      p.out.q_row[b] = 0;
+      for (int k = 0; k < nd; ++k) {
+        p.out.drafts[b * nd + k] = -1;
+        p.out.q_x[b * nd + k] = 0.f;
+        p.out.q_m[b * nd + k] = 0.f;
+        p.out.q_s[b * nd + k] = 0.f;
+      }
+    }
+    if (p.resid_mass) p.resid_mass[b] = (a < n) ? s_mass : -1.f;
+    if (p.p_x)
+      for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = d.px[k];
+    if (p.row_m)
+      for (int r = 0; r < p.rows; ++r) {
+        const bool rd = r < n + N;
+        p.row_m[b * p.rows + r] = rd ? d.M[r] : NAN;
+        p.row_s[b * p.rows + r] = rd ? d.S[r] : NAN;
+      }
+  }
+}
+
+}  // namespace isd
+
+// ================================================================ host API
+namespace {
+using namespace isd;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+struct AcceptLayout {
+  int nch, ns;
+  size_t stats_off, resid_off, samp_off, total;
+};
+
+AcceptLayout accept_layout(int C, int N, int V, int rows) {
+  AcceptLayout L;
+  L.nch = (V + kChunk - 1) / kChunk;
+  L.ns = L.nch > N ? L.nch : N;
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  L.stats_off = 0;
+  L.resid_off = up(static_cast<size_t>(C) * rows * L.nch * sizeof(float2));
+  L.samp_off = L.resid_off + up(static_cast<size_t>(C) * L.ns * sizeof(float));
+  L.total = L.samp_off + up(static_cast<size_t>(C) * N * sizeof(int2));
+  return L;
+}
+
+bool state_ok(const isd_seq_state& s) { return s.n_draft && s.drafts && s.q_x && s.q_m && s.q_s && s.q_row; }
+
+template <typename E>
+hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_stats_kernel<E>, dim3(p.nch, 2 * p.N - 1, p.C), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(accept_sample_kernel<E>, dim3(p.ns, p.C), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(accept_finish_kernel<E>, dim3(p.C), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t isd_accept_workspace_size(int C, int N, int V, int rows) {
+  if (C < 0 || N < 2 || N > kMaxN || V < 1 || rows < 2 * N - 1) return 0;
+  return accept_layout(C, N, V, rows).total;
+}
+
+int isd_accept(const isd_accept_args* a, hipStream_t stream) {
+  if (!a) return ISD_E_INVALID;
+  if (a->C < 0 || a->N < 2 || a->V < 1) return ISD_E_INVALID;
+  if (a->C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
+  if (a->N > kMaxN) return ISD_E_UNSUPPORTED;
+  if (a->rows < 2 * a->N - 1) return ISD_E_INVALID;
+  if (a->dtype != ISD_BF16 && a->dtype != ISD_F32) return ISD_E_UNSUPPORTED;
+  if (a->C == 0) return ISD_OK;
+  if (!a->logits || !state_ok(a->in) || !state_ok(a->out)) return ISD_E_INVALID;
+  if (!a->accepted || !a->n_emit || !a->emit || !a->kv_commit) return ISD_E_INVALID;
+  if ((a->row_m == nullptr) != (a->row_s == nullptr)) return ISD_E_INVALID;
+  const int esz = a->dtype == ISD_BF16 ? 2 : 4;
+  if (a->ld < a->V || (a->ld * esz) % 16 != 0) return ISD_E_INVALID;
+  if (!aligned16(a->logits) || (a->prev_logits && !aligned16(a->prev_logits))) return ISD_E_INVALID;
+  if (a->in.n_draft == a->out.n_draft || a->in.drafts == a->out.drafts || a->in.q_x == a->out.q_x ||
+      a->in.q_m == a->out.q_m || a->in.q_s == a->out.q_s || a->in.q_row == a->out.q_row)
+    return ISD_E_INVALID;
+  const AcceptLayout L = accept_layout(a->C, a->N, a->V, a->rows);
+  if (!a->ws || a->ws_bytes < L.total || !aligned16(a->ws)) return ISD_E_WORKSPACE;
+  int rc = isd_check_device_internal();
+  if (rc) return rc;
+
+  AcceptParams p;
+  p.logits = a->logits;
+  p.prev_logits = a->prev_logits;
+  p.ld = static_cast<long>(a->ld);
+  p.C = a->C;
+  p.N = a->N;
+  p.V = a->V;
+  p.rows = a->rows;
+  p.nch = L.nch;
+  p.ns = L.ns;
+  p.in = a->in;
+  p.out = a->out;
+  p.seed = a->seed;
+  p.step = a->step;
+  p.accepted = a->accepted;
+  p.n_emit = a->n_emit;
+  p.emit = a->emit;
+  p.kv_commit = a->kv_commit;
+  p.p_x = a->p_x;
+  p.resid_mass = a->resid_mass;
+  p.row_m = a->row_m;
+  p.row_s = a->row_s;
+  char* ws = static_cast<char*>(a->ws);
+  p.stats = reinterpret_cast<float2*>(ws + L.stats_off);
+  p.resid = reinterpret_cast<float*>(ws + L.resid_off);
+  p.samp = reinterpret_cast<int2*>(ws + L.samp_off);
+  p.dev_err = a->dev_err;
+  const hipError_t e = a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, stream) : launch_accept<float>(p, stream);
+  return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,230 @@
+/*
+ * isd.h - C ABI of the Introspective Strided Decoding (ISD) step on MI355X.
+ *
+ * One ISD step of an I-DLM model runs a single causal forward over a stride
+ * block of 2N rows: it verifies the N-1 drafts proposed on the previous step
+ * with the min(1, p(x)/q(x)) test and proposes new tokens at MASK positions
+ * (I-DLM - Modeles de langage a diffusion introspective, fr.news.hada.io,
+ * sections "Methodologie d'I-DLM > Introspective Strided Decoding (ISD)" and
+ * "Documentation et ressources > Inference & ISD"). This library implements
+ * the data-parallel hot path of that step for one GPU (gfx950):
+ *
+ *   isd_kv_write      put the block's K/V rows into the paged cache
+ *   isd_attention     causal GQA attention of the block over the pages
+ *   isd_accept        vocab softmax, p/q test, residual / bonus draw, proposals
+ *   isd_linear        y = x W^T (bf16 in, fp32 out), the base projection
+ *   gated_lora_apply  y += s (x A^T) B^T on MASK rows only (R-ISD)
+ *   isd_linear_gated  both of the above in one pass
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is device memory owned by the caller, except
+ *     the struct pointers themselves (host memory, read during the call).
+ *     The library never allocates device memory; calls that need scratch
+ *     space take a caller-provided workspace and publish its size.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and
+ *     never synchronises. Calls are stateless and thread-safe; two calls that
+ *     share a workspace must not overlap.
+ *   - Return value: ISD_OK, or a negative ISD_E_* code when an argument is
+ *     invalid or unsupported (checked on the host before any launch) or a
+ *     launch fails. isd_strerror() gives the text.
+ *   - Problems only the device can see (a page id outside the pool, a
+ *     position beyond a sequence's block table, a non-finite logits row, a
+ *     draft id outside the vocabulary, an invalid per-sequence state) are
+ *     ORed as ISD_DEV_* bits into *dev_err when dev_err is not NULL; kernels
+ *     never trap. The caller clears dev_err.
+ *   - Element types: ISD_BF16 (bfloat16 bits in uint16) or ISD_F32.
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ codes */
+#define ISD_OK 0
+#define ISD_E_INVALID (-1)     /* null pointer, size or stride out of range */
+#define ISD_E_UNSUPPORTED (-2) /* dtype, head_dim, stride, rank or shape not built */
+#define ISD_E_WORKSPACE (-3)   /* workspace missing or too small */
+#define ISD_E_LAUNCH (-4)      /* the HIP runtime refused a launch */
+#define ISD_E_DEVICE (-5)      /* the current device is not a gfx950 GPU */
+
+#define ISD_DEV_PAGE_OOB 1u    /* block-table entry outside [0, num_pages) */
+#define ISD_DEV_CAPACITY 2u    /* position beyond the block table's columns */
+#define ISD_DEV_NONFINITE 4u   /* a logits row read by isd_accept holds NaN/Inf */
+#define ISD_DEV_TOKEN_OOB 8u   /* a pending draft id outside [0, V) */
+#define ISD_DEV_STATE 16u      /* n_draft or q_row out of range */
+
+#define ISD_BF16 1
+#define ISD_F32 2
+
+#define ISD_PAGE_SIZE 16 /* tokens per KV page */
+
+const char* isd_strerror(int code);
+/* Library version as 10000*major + 100*minor + patch. */
+int isd_version(void);
+
+/* --------------------------------------------------------- KV cache
+ * Paged KV cache (I-DLM page, "Documentation et ressources > Serving
+ * (SGLang)": paged KV and an attention kernel that reads only from pages).
+ *
+ * Physical layout of one page, chosen so that every MFMA operand the
+ * attention kernel needs is a run of 16 contiguous bytes:
+ *   K: [num_kv_heads][head_dim / KP][16 slots][KP]    KP = 16 / sizeof(elem)
+ *   V: [num_kv_heads][head_dim][16 slots]
+ * i.e. for bf16, element (slot s, head g, dim d) of page p is at
+ *   k_pages[((p*Hkv + g)*(D/8) + d/8)*16*8 + s*8 + d%8]
+ *   v_pages[((p*Hkv + g)*D + d)*16 + s].
+ * Position t of sequence b lives in page block_table[b*table_stride + t/16],
+ * slot t%16. Entries of the block table past a sequence's length are never
+ * read.
+ */
+typedef struct isd_kv_cache {
+  void* k_pages;              /* num_pages * Hkv * D * 16 elements */
+  void* v_pages;              /* num_pages * Hkv * D * 16 elements */
+  const int32_t* block_table; /* [C][table_stride] physical page ids */
+  int32_t table_stride;       /* columns of block_table (max pages per sequence) */
+  int32_t num_pages;          /* pages in each pool */
+  int32_t page_size;          /* must be ISD_PAGE_SIZE */
+  int32_t num_kv_heads;       /* Hkv, 1..64 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t dtype;              /* ISD_BF16 or ISD_F32 */
+} isd_kv_cache;
+
+/* Write K/V rows into the pages: row r < nrows[b] of sequence b goes to
+ * position pos0[b] + r. k and v are [C][rows][Hkv][D] in kv->dtype.
+ * nrows may be NULL (every sequence writes `rows` rows). Positions whose
+ * page column is >= table_stride or whose page id is outside the pool are
+ * skipped and flagged (ISD_DEV_CAPACITY / ISD_DEV_PAGE_OOB). */
+int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
+                 const int32_t* pos0, const int32_t* nrows, int C, int rows,
+                 int32_t* dev_err, hipStream_t stream);
+
+/* ------------------------------------------------------- attention
+ * Causal grouped-query attention of the stride block over the paged cache
+ * (strict causality: I-DLM page, "Methodologie d'I-DLM > Serving compatible
+ * AR"). Row i of sequence b sits at position ctx[b] + i and attends to
+ * positions 0 .. ctx[b] + i, all read from pages: the block's own K/V must
+ * have been written with isd_kv_write first.
+ *
+ *   q    [C][rows][Hq][D] in kv->dtype
+ *   out  [C][rows][Hq][D] fp32 (normalised attention output)
+ *   ctx  [C] cached tokens before the block
+ *   Query head h reads KV head h / (Hq / Hkv). scale multiplies q.k
+ *   (1/sqrt(D) in the usual model). max_len is a host-side upper bound of
+ *   ctx[b] + rows over the batch; it sizes the grid. chunk (0 = automatic,
+ *   else a multiple of 32) is the KV span one workgroup reduces before a
+ *   log-sum-exp merge; the workspace size depends on it.
+ * Supported: D in {64, 128}; Hq multiple of Hkv; (Hq/Hkv)*rows <= 128;
+ * rows <= 64.
+ */
+size_t isd_attention_workspace_size(int C, int rows, int num_q_heads,
+                                    const isd_kv_cache* kv, int max_len,
+                                    int chunk);
+int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx,
+                  int C, int rows, int num_q_heads, float scale, int max_len,
+                  int chunk, float* out, void* ws, size_t ws_bytes,
+                  int32_t* dev_err, hipStream_t stream);
+
+/* ---------------------------------------------------------- accept
+ * Per-sequence decoding state carried from step to step. Draft j (1-based)
+ * was proposed from row q_row + j - 1 of the previous step's block; q_x is
+ * its probability under that row and (q_m, q_s) are that row's max logit
+ * and sum of exp(l - q_m).
+ */
+typedef struct isd_seq_state {
+  int32_t* n_draft; /* [C] pending drafts: 0 (FRESH) .. N-1 (FULL) */
+  int32_t* drafts;  /* [C][N-1] draft token ids */
+  float* q_x;       /* [C][N-1] Q_j(x_j) */
+  float* q_m;       /* [C][N-1] */
+  float* q_s;       /* [C][N-1] */
+  int32_t* q_row;   /* [C] */
+} isd_seq_state;
+
+/* The accept side of one step (I-DLM page, "Documentation et ressources >
+ * Inference & ISD": proposals q at MASK positions, verification p at clean
+ * positions, keep x with probability min(1, p(x)/q(x))). For each sequence
+ * with n = n_draft pending drafts, rows 0..n of the block are clean and rows
+ * n+1.. are MASK rows (logit shift: row i predicts position ctx + i + 1):
+ *   1. P_j = softmax(logits row j) in fp32 from the bf16/f32 logits.
+ *   2. for j = 1..n: accept x_j iff u_j * q_x_j < P_{j-1}(x_j); a = number
+ *      accepted before the first rejection.
+ *   3. a < n: draw t from normalize(max(0, P_a - Q_{a+1})) (P_a if that mass
+ *      is 0), next state FRESH (n_draft = 0).
+ *      a = n: draw the bonus t from P_n and N-1 new drafts from rows
+ *      n+1..n+N-1, next state FULL (n_draft = N-1, q_row = n+1).
+ *   4. emit = (x_1..x_a, t), n_emit = kv_commit = a + 1.
+ * Draws are inverse-CDF over ascending token ids with u from Philox4x64-10:
+ * key (seed, 0), counter (slot, b, step, 0), u = ((w0>>41) + 0.5) * 2^-23;
+ * slots 1..N-1 test drafts, slot N draws t, slot N+k draws proposal k.
+ * A sequence whose step cannot be taken (non-finite row, bad draft id or
+ * state) gets accepted = -1, n_emit = kv_commit = 0, emit = -1 and its state
+ * copied unchanged, and a bit in dev_err.
+ */
+typedef struct isd_accept_args {
+  int32_t C;     /* sequences, <= 65535 */
+  int32_t N;     /* stride, 2..8 */
+  int32_t V;     /* vocabulary size */
+  int32_t rows;  /* rows per block in logits (>= 2N-1, usually 2N) */
+  int32_t dtype; /* logits element type */
+  const void* logits;      /* [C][rows][ld] this step's block */
+  const void* prev_logits; /* [C][rows][ld] previous block; NULL if no drafts */
+  int64_t ld;              /* elements between rows, >= V, 16-byte aligned */
+  isd_seq_state in;        /* read only */
+  isd_seq_state out;       /* written; must not alias `in` */
+  uint64_t seed;
+  uint64_t step;
+  int32_t* accepted;  /* [C] a, or -1 */
+  int32_t* n_emit;    /* [C] */
+  int32_t* emit;      /* [C][N], -1 past n_emit */
+  int32_t* kv_commit; /* [C] */
+  float* p_x;         /* optional [C][N-1]: P_{j-1}(x_j) of tested drafts */
+  float* resid_mass;  /* optional [C]: sum max(0, P_a - Q_{a+1}), or -1 */
+  float* row_m;       /* optional [C][rows]: max logit of each row read */
+  float* row_s;       /* optional [C][rows]: sum exp(l - row_m) */
+  void* ws;
+  size_t ws_bytes;
+  int32_t* dev_err;
+} isd_accept_args;
+
+size_t isd_accept_workspace_size(int C, int N, int V, int rows);
+int isd_accept(const isd_accept_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------ projections
+ * Base projection of the model and the gated LoRA of lossless R-ISD
+ * (I-DLM page, "Speedup Factor Explorer" and "Documentation et ressources >
+ * Lossless R-ISD": the adapter acts only at MASK positions so clean
+ * positions stay bit-identical to the base model).
+ *
+ * isd_linear: y[M][Nout] (fp32) = x[M][K] W[Nout][K]^T with bf16 x and W.
+ * Each output's reduction order depends only on K, never on M, on the other
+ * rows or on their mask.
+ * gated_lora_apply: y[m] += scale * (x[m] A^T) B^T for rows with
+ * is_mask[m] != 0; A [r][K] and B [Nout][r] bf16; other rows are never
+ * written. Needs a workspace of isd_lora_workspace_size(M, r) bytes.
+ * isd_linear_gated: y = isd_linear(x, W) then gated_lora_apply in one pass;
+ * its clean rows equal isd_linear's bit for bit.
+ * Supported: K multiple of 64; r multiple of 16, <= 128; M, Nout >= 1.
+ */
+int isd_linear(const void* x, const void* W, int M, int K, int Nout,
+               float* y, hipStream_t stream);
+size_t isd_lora_workspace_size(int M, int r);
+int gated_lora_apply(const void* x, const void* A, const void* B,
+                     const uint8_t* is_mask, int M, int K, int Nout, int r,
+                     float scale, float* y, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+int isd_linear_gated(const void* x, const void* W, const void* A,
+                     const void* B, const uint8_t* is_mask, int M, int K,
+                     int Nout, int r, float scale, float* y, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISD_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports what include/isd.h declares, and rejects
+invalid arguments on the host (no GPU needed: these checks run before any
+HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verify_decoding_amd as dvd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dvd.LIB_PATH):
+        pytest.fail("libisd.so is not built (run __graft_entry__.build())")
+    return dvd.lib()
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    for n in ["isd_kv_write", "isd_attention", "isd_attention_workspace_size", "isd_accept",
+              "isd_accept_workspace_size", "isd_linear", "gated_lora_apply", "isd_linear_gated",
+              "isd_lora_workspace_size", "isd_strerror", "isd_version"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    handle = ctypes.CDLL(dvd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+
+
+def test_strerror_and_version(lib):
+    assert dvd.strerror(0) == "success"
+    for code in (-1, -2, -3, -4, -5):
+        assert dvd.strerror(code) != "unknown error code"
+    assert lib.isd_version() >= 100
+
+
+def test_attention_rejects_bad_arguments_on_host(lib):
+    null_kv = lib.isd_attention(None, None, None, 1, 8, 4, 0.1, 64, 0, None, None, 0, None, None)
+    assert null_kv == -1
+    kv = dvd.IsdKvCache(16, 16, 16, 4, 10, 16, 1, 96, dvd.ISD_BF16)  # head_dim 96 unsupported
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    kv.head_dim = 128
+    kv.page_size = 8
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    kv.page_size = 16
+    # Hq not a multiple of Hkv
+    kv.num_kv_heads = 3
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    kv.num_kv_heads = 1
+    # group * rows > 128
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 40, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    # scale must be positive, chunk a multiple of 32, max_len >= rows
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, -1.0, 64, 0, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 48, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4, 0, 16, None, 0, None, None) == -1
+    # misaligned q
+    assert lib.isd_attention(ctypes.byref(kv), 18, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -1
+    # a split that needs a workspace and gets none
+    need = lib.isd_attention_workspace_size(1, 8, 4, ctypes.byref(kv), 4096, 64)
+    assert need > 0
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, None, 0, None, None) == -3
+    assert lib.isd_attention_workspace_size(1, 8, 4, ctypes.byref(kv), 64, 64) == 0
+
+
+def test_accept_rejects_bad_arguments_on_host(lib):
+    assert lib.isd_accept(None, None) == -1
+    a = dvd.IsdAcceptArgs()
+    a.C, a.N, a.V, a.rows, a.dtype = 2, 9, 100, 18, dvd.ISD_BF16
+    assert lib.isd_accept(ctypes.byref(a), None) == -2  # N > 8
+    a.N, a.rows = 4, 6
+    assert lib.isd_accept(ctypes.byref(a), None) == -1  # rows < 2N - 1
+    a.rows = 8
+    assert lib.isd_accept(ctypes.byref(a), None) == -1  # null pointers
+    fake = 1 << 20
+    st_in = dvd.IsdSeqState(*(fake + 64 * i for i in range(6)))
+    st_out = dvd.IsdSeqState(*(fake + 4096 + 64 * i for i in range(6)))
+    a.logits, a.in_, a.out = fake, st_in, st_out
+    a.accepted, a.n_emit, a.emit, a.kv_commit = fake, fake, fake, fake
+    a.ld = 100
+    assert lib.isd_accept(ctypes.byref(a), None) == -1  # 200-byte rows are not 16-byte aligned
+    a.ld = 104
+    assert lib.isd_accept(ctypes.byref(a), None) == -3  # no workspace
+    a.out = st_in
+    assert lib.isd_accept(ctypes.byref(a), None) == -1  # out aliases in
+    assert lib.isd_accept_workspace_size(64, 4, 151936, 8) > 0
+    assert lib.isd_accept_workspace_size(64, 1, 151936, 8) == 0
+
+
+def test_linear_rejects_bad_arguments_on_host(lib):
+    assert lib.isd_linear(16, 16, 4, 100, 8, 16, None) == -2  # K not a multiple of 64
+    assert lib.isd_linear(None, 16, 4, 64, 8, 16, None) == -1
+    assert lib.isd_linear(16, 16, 0, 64, 8, 16, None) == 0  # empty problem
+    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, 16, 1 << 20, None) == -2  # rank 24
+    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 16, 8, None) == -3  # ws too small
+    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4

@@ -1,0 +1,154 @@
+"""GPU parity of isd_kv_write and isd_attention against the oracle.
+
+Tolerance: the pass criterion is 2e-3 relative for attention outputs (bf16
+inputs, fp32 accumulation), read normwise per (sequence, query head) slab:
+max |O - O*| / max |O*| over its rows x D. fp32 inputs are held to 1e-5.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import draft_verify_decoding_amd as dvd
+import workload
+from oracle import attention as ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def to64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def fill_cache(case):
+    kv = dvd.KVCache(case.num_pages, case.Hkv, case.D, case.dtype, torch.from_numpy(case.table), DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dvd.isd_kv_write(kv, case.k_rows.to(DEV).contiguous(), case.v_rows.to(DEV).contiguous(),
+                     torch.zeros(case.C, dtype=torch.int32, device=DEV),
+                     torch.from_numpy(case.lengths.astype(np.int32)).to(DEV), dev_err=err)
+    return kv, err
+
+
+def oracle_pages(case):
+    kp = np.zeros((case.num_pages, 16, case.Hkv, case.D))
+    vp = np.zeros_like(kp)
+    ref.kv_write(kp, vp, case.table, np.zeros(case.C, int), to64(case.k_rows), to64(case.v_rows), case.lengths)
+    return kp, vp
+
+
+def slab_errors(got, want):
+    """max |got - want| / max |want| per (sequence, head)."""
+    C, R, H, D = want.shape
+    g = got.transpose(0, 2, 1, 3).reshape(C, H, R * D)
+    w = want.transpose(0, 2, 1, 3).reshape(C, H, R * D)
+    return np.abs(g - w).max(-1) / np.abs(w).max(-1)
+
+
+def run(case, chunk=0, seqs=None):
+    print(f"attention case C={case.C} rows={case.rows} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
+          f"{case.dtype} chunk={chunk}", flush=True)
+    kv, err = fill_cache(case)
+    out = dvd.isd_attention(kv, case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV),
+                            max_len=int(case.lengths.max()), chunk=chunk, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    got = out.cpu().double().numpy()
+    kp, vp = oracle_pages(case)
+    q64 = to64(case.q)
+    if seqs is None:
+        want = ref.block_attention(q64, kp, vp, case.table, case.ctx)
+        return got, want
+    want = ref.block_attention(q64[seqs], kp, vp, case.table[seqs], case.ctx[seqs])
+    return got[seqs], want
+
+
+def test_kv_write_matches_documented_page_layout():
+    case = workload.AttentionCase(3, C=3, rows=8, Hq=8, Hkv=2, D=128, ctx=[0, 21, 50], spare_pages=3)
+    kv, err = fill_cache(case)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    kp, vp = oracle_pages(case)  # [P, 16, Hkv, D] plain layout
+    P, Hkv, D = case.num_pages, case.Hkv, case.D
+    k_dev = to64(kv.k_pages).reshape(P, Hkv, D // 8, 16, 8)
+    v_dev = to64(kv.v_pages).reshape(P, Hkv, D, 16)
+    used = sorted(set(case.table[case.table >= 0].ravel().tolist()))
+    for b in range(case.C):
+        for t in range(int(case.lengths[b])):
+            p, s = case.table[b, t // 16], t % 16
+            assert np.array_equal(k_dev[p, :, :, s, :].reshape(Hkv, D), kp[p, s])
+            assert np.array_equal(v_dev[p, :, :, s], vp[p, s])
+    unused = sorted(set(range(P)) - set(used))
+    assert unused and not k_dev[unused].any()
+
+
+def test_tiny_fp32_config():
+    """C=1, 8 rows (N=4), 4 query heads, 1 KV head, D=64, 128 cached, fp32."""
+    case = workload.AttentionCase(0, C=1, rows=8, Hq=4, Hkv=1, D=64, ctx=128, dtype=torch.float32)
+    got, want = run(case)
+    assert slab_errors(got, want).max() < 1e-5
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 96])
+def test_bf16_gqa_ragged_contexts(chunk):
+    """8B-class heads (32/8, D=128), several tiles, ragged tails, split-KV."""
+    case = workload.AttentionCase(11, C=5, rows=8, Hq=32, Hkv=8, D=128, ctx=[0, 1, 31, 100, 1000])
+    got, want = run(case, chunk=chunk)
+    e = slab_errors(got, want)
+    print("max slab error", e.max())
+    assert e.max() < 2e-3
+
+
+@pytest.mark.parametrize("N", [2, 3, 6, 8])
+def test_32b_class_heads_strides(N):
+    """64/8 heads: the GQA pack is 8 * 2N query rows (16..128)."""
+    case = workload.AttentionCase(20 + N, C=2, rows=2 * N, Hq=64, Hkv=8, D=128, ctx=[333, 1290])
+    got, want = run(case, chunk=256)
+    assert slab_errors(got, want).max() < 2e-3
+
+
+def test_head_dim_64_bf16_and_single_token_context():
+    case = workload.AttentionCase(31, C=3, rows=8, Hq=8, Hkv=2, D=64, ctx=[0, 5, 77])
+    got, want = run(case)
+    assert slab_errors(got, want).max() < 2e-3
+    # row 0 of a sequence without context sees exactly its own value row
+    v0 = to64(case.v_rows[0, 0])
+    for h in range(8):
+        assert np.allclose(got[0, 0, h], v0[h // 4], rtol=1e-6, atol=1e-6)
+
+
+def test_largest_query_pack_and_rows():
+    """rows = 64 with group 2 (128 query columns)."""
+    case = workload.AttentionCase(41, C=2, rows=64, Hq=4, Hkv=2, D=128, ctx=[10, 300])
+    got, want = run(case, chunk=128)
+    assert slab_errors(got, want).max() < 2e-3
+
+
+def test_stationary_batch_shapes_sampled():
+    """C=64, N=4, 32/8 heads, D=128, contexts U{1024..8192}, 16-token pages in
+    a shuffled pool: the whole batch runs, 6 sampled sequences are checked."""
+    case = workload.AttentionCase(3, C=64, rows=8, Hq=32, Hkv=8, D=128, ctx=("uniform", 1024, 8192))
+    seqs = np.array([0, 9, 17, 31, 48, 63])
+    got, want = run(case, seqs=seqs)
+    assert slab_errors(got, want).max() < 2e-3
+
+
+def test_outputs_are_deterministic():
+    case = workload.AttentionCase(5, C=4, rows=8, Hq=32, Hkv=8, D=128, ctx=[700, 2000, 64, 3000])
+    kv, err = fill_cache(case)
+    q, ctx = case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV)
+    a = dvd.isd_attention(kv, q, ctx, max_len=3008, chunk=256)
+    b = dvd.isd_attention(kv, q, ctx, max_len=3008, chunk=256)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_bad_page_id_sets_device_flag():
+    case = workload.AttentionCase(6, C=2, rows=8, Hq=8, Hkv=2, D=128, ctx=[40, 40])
+    kv, err = fill_cache(case)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    kv.block_table[1, 1] = case.num_pages + 5
+    dvd.isd_attention(kv, case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV), max_len=48, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & dvd.DEV_PAGE_OOB
