@@ -1,0 +1,403 @@
+"""Throughput of the ISD step on one MI355X.
+
+Workload (stationary batch, 8B-class shapes): C = 64 sequences, stride N = 4
+(8-row blocks: 4 verify + 4 MASK), 36 layers of grouped-query attention with
+32 query heads, 8 KV heads, head_dim 128, bf16 paged KV cache in 16-token
+pages placed by a seeded shuffle, cached contexts drawn uniformly from
+1024..8192 per sequence, vocabulary 151,936 with draft noise set for a mean
+acceptance of 0.9, gated-LoRA (rank 32 per projection) Q/K/V/O projections
+on the 512 block rows of each layer (Q, K and V fused into one 6144-wide
+projection). All inputs are seeded synthetic tensors (no weights or
+datasets exist for this), resident in HBM before the timed region.
+
+One step = for each of the 36 layers: gated fused QKV projection, KV write of
+the block, block attention over the pages, gated O projection; then the
+accept step over the block logits (verify, residual / bonus draw, proposals,
+KV commit). The MLP and the LM head are not part of the library; the logits
+the LM head would produce are synthetic and pre-generated per step.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ISD accepted tokens/s at C=64,N=4 (8B shapes); attn+accept HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+
+CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, lora_rank=32,
+           ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_bytes(ctx, cfg):
+    """Algorithmic HBM bytes of one isd_attention call: every K and V element
+    of positions 0..ctx_b + 2N - 1 once (bf16), the queries (bf16) and the
+    fp32 outputs."""
+    R = 2 * cfg["N"]
+    kv = int(np.sum(ctx + R)) * cfg["Hkv"] * cfg["D"] * 2 * 2
+    q = cfg["C"] * R * cfg["Hq"] * cfg["D"] * 2
+    o = cfg["C"] * R * cfg["Hq"] * cfg["D"] * 4
+    return kv + q + o
+
+
+def accept_bytes(n_draft, accepted, cfg):
+    """Algorithmic HBM bytes of one accept step: each logits row the step
+    reads once (rows 0..n+N-1 per sequence, bf16), plus the two rows of the
+    residual (P_a and the old Q_{a+1}) for sequences that rejected a draft."""
+    V, N = cfg["V"], cfg["N"]
+    rows = int(np.sum(n_draft + N))
+    resid = int(np.sum(accepted < n_draft)) * 2
+    return (rows + resid) * V * 2
+
+
+def build(cfg, steps_total, dev):
+    import draft_verify_decoding_amd as dvd
+    import workload
+
+    C, N, Hq, Hkv, D, L = cfg["C"], cfg["N"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    R = 2 * N
+    seed = cfg["seed"]
+    ctx0 = workload.contexts(seed, C, cfg["ctx"])
+    capacity = ctx0 + R + steps_total * N + 16
+    table, num_pages = workload.block_table(seed, capacity)
+    table_t = torch.from_numpy(table)
+    log(f"[bench] {L} layers x {num_pages} pages; KV pool {2 * L * num_pages * Hkv * D * 16 * 2 / 1e9:.1f} GB")
+
+    # KV pools: fill every layer from one random source (values do not
+    # change the work; every layer still lives in its own HBM pages)
+    per_pool = num_pages * Hkv * D * 16
+    src = workload.normal((per_pool,), 1.0, torch.bfloat16, dev, seed, "kv-src")
+    kvs = []
+    for _ in range(L):
+        kv = dvd.KVCache(num_pages, Hkv, D, torch.bfloat16, table_t, dev)
+        kv.k_pages.copy_(src)
+        kv.v_pages.copy_(src.flip(0))
+        kvs.append(kv)
+    del src
+
+    M, H, r = C * R, cfg["hidden"], cfg["lora_rank"]
+    mask = torch.from_numpy(workload.stride_mask(M, N).astype(np.uint8)).to(dev)
+    layers = []
+    for l in range(L):
+        lay = dict(
+            q=workload.normal((C, R, Hq, D), 1.0, torch.bfloat16, dev, seed, "q", l),
+            k=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "kb", l),
+            v=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "vb", l),
+            x=workload.normal((M, H), 1.0, torch.bfloat16, dev, seed, "x", l),
+            xo=workload.normal((M, H), 1.0, torch.bfloat16, dev, seed, "xo", l),
+            out=torch.empty((C, R, Hq, D), dtype=torch.float32, device=dev),
+        )
+        # Q, K and V run as one projection (weights stacked, 6144 outputs);
+        # their three rank-r adapters stack into A [3r, H] and a block-
+        # diagonal B [6144, 3r], which is the same delta on each slice.
+        proj = {}
+        parts = [("q", Hq * D), ("k", Hkv * D), ("v", Hkv * D)]
+        Ws, As, Bs = [], [], []
+        for name, nout in parts:
+            Ws.append(workload.normal((nout, H), 0.02, torch.bfloat16, dev, seed, "W", name, l))
+            As.append(workload.normal((r, H), 0.01, torch.bfloat16, dev, seed, "A", name, l))
+            Bs.append(workload.normal((nout, r), 0.01, torch.bfloat16, dev, seed, "B", name, l))
+        n_qkv = sum(n for _, n in parts)
+        Bqkv = torch.zeros((n_qkv, 3 * r), dtype=torch.bfloat16, device=dev)
+        off = 0
+        for i, (_, nout) in enumerate(parts):
+            Bqkv[off:off + nout, i * r:(i + 1) * r] = Bs[i]
+            off += nout
+        proj["qkv"] = dict(W=torch.cat(Ws).contiguous(), A=torch.cat(As).contiguous(), B=Bqkv,
+                           y=torch.empty((M, n_qkv), dtype=torch.float32, device=dev))
+        proj["o"] = dict(W=workload.normal((H, H), 0.02, torch.bfloat16, dev, seed, "W", "o", l),
+                         A=workload.normal((r, H), 0.01, torch.bfloat16, dev, seed, "A", "o", l),
+                         B=workload.normal((H, r), 0.01, torch.bfloat16, dev, seed, "B", "o", l),
+                         y=torch.empty((M, H), dtype=torch.float32, device=dev))
+        lay["proj"] = proj
+        layers.append(lay)
+    lora_ws = torch.empty(dvd.isd_lora_workspace_size(M, 3 * r), dtype=torch.uint8, device=dev)
+    return dict(ctx0=ctx0, kvs=kvs, layers=layers, mask=mask, lora_ws=lora_ws, table=table)
+
+
+def dry_run(cfg, steps_total, ctx0, dev):
+    """Accept-only pass that fixes the trajectory: the logits of every step
+    (drawn from the synthetic teacher given the state) are kept in HBM, with
+    the per-step contexts, draft counts and accepted lengths."""
+    import draft_verify_decoding_amd as dvd
+    import workload
+
+    C, N, V = cfg["C"], cfg["N"], cfg["V"]
+    R = 2 * N
+    sigma_q = workload.SIGMA_Q_V151936[cfg["accept"]]
+    teacher = workload.TeacherLogits(cfg["seed"], C, V, steps_total * N + R + 1, cfg["sigma_l"], sigma_q,
+                                     torch.bfloat16, dev)
+    ctx0_t = torch.from_numpy(ctx0.astype(np.int64)).to(dev)
+    ctx = torch.from_numpy(ctx0.astype(np.int32)).to(dev)
+    s_in, s_out = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
+    ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
+    logits, ctxs, nds, accs = [], [], [], []
+    prev = None
+    for t in range(steps_total):
+        lg = teacher.block(t, ctx.long(), ctx0_t, s_in.n_draft.long(), R).contiguous()
+        ctxs.append(ctx.cpu().numpy().copy())
+        nds.append(s_in.n_draft.cpu().numpy().copy())
+        out = dvd.isd_accept(lg, prev, s_in, s_out, N, cfg["seed"], t, ws=ws, ctx=ctx)
+        accs.append(out.accepted.cpu().numpy().copy())
+        logits.append(lg)
+        prev = lg
+        s_in, s_out = s_out, s_in
+    final_ctx = ctx.cpu().numpy().copy()
+    del teacher
+    torch.cuda.synchronize()
+    return logits, np.array(ctxs), np.array(nds), np.array(accs), final_ctx
+
+
+def cpu_baseline(cfg, budget_layers=24, accept_seqs=16, accept_steps=8):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    (a) block attention + gated Q/K/V/O projections of one sequence at the
+    workload's mean context for `budget_layers` of the 36 layers, scaled to
+    36; (b) the accept step for `accept_seqs` sequences over `accept_steps`
+    steps from FRESH at the full vocabulary. Returns tokens/s."""
+    import workload
+    from oracle import accept as oacc
+    from oracle import attention as oatt
+    from oracle import lora as olora
+    from oracle import philox
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    C, N, Hq, Hkv, D, V = cfg["C"], cfg["N"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["V"]
+    R, H, r = 2 * N, cfg["hidden"], cfg["lora_rank"]
+    ctx_mean = int(np.mean(workload.contexts(cfg["seed"], C, cfg["ctx"])))
+
+    t_fwd = 0.0
+    for l in range(budget_layers):
+        case = workload.AttentionCase(cfg["seed"] + 100 + l, C=1, rows=R, Hq=Hq, Hkv=Hkv, D=D, ctx=ctx_mean)
+        kp = np.zeros((case.num_pages, 16, Hkv, D))
+        vp = np.zeros_like(kp)
+        oatt.kv_write(kp, vp, case.table, [0], case.k_rows.double().numpy(), case.v_rows.double().numpy(),
+                      case.lengths)
+        q = case.q.double().numpy()
+        mats = []
+        for name, nout in (("q", Hq * D), ("k", Hkv * D), ("v", Hkv * D), ("o", H)):
+            x, W, A, B = (t.double().numpy() for t in workload.lora_case(cfg["seed"] + l, R, H, nout, r))
+            mats.append((x, W, A, B))
+        mask = workload.stride_mask(R, N)
+        t0 = time.perf_counter()
+        oatt.block_attention(q, kp, vp, case.table, case.ctx)
+        for x, W, A, B in mats:
+            olora.gated_lora(x, W, A, B, mask, 1.0)
+        t_fwd += time.perf_counter() - t0
+    t_fwd_seq_step = t_fwd / budget_layers * cfg["layers"]
+
+    sigma_q = workload.SIGMA_Q_V151936[cfg["accept"]]
+    teacher = workload.TeacherLogits(cfg["seed"], accept_seqs, V, accept_steps * N + R + 1, cfg["sigma_l"],
+                                     sigma_q, torch.bfloat16, "cpu")
+    ctx0 = torch.zeros(accept_seqs, dtype=torch.int64)
+    ctx = ctx0.clone()
+    n = np.zeros(accept_seqs, np.int64)
+    drafts = np.full((accept_seqs, N - 1), -1, np.int64)
+    qrow = np.zeros(accept_seqs, np.int64)
+    prev = None
+    tokens = 0
+    t_acc = 0.0
+    for t in range(accept_steps):
+        lg = teacher.block(t, ctx, ctx0, torch.from_numpy(n), R).double().numpy()
+        u = philox.step_uniforms(cfg["seed"], t, accept_seqs, N)
+        t0 = time.perf_counter()
+        o = oacc.accept_step(lg, prev, n, drafts, qrow, u, N)
+        t_acc += time.perf_counter() - t0
+        tokens += int(o["n_emit"].sum())
+        ctx += torch.from_numpy(o["kv_commit"])
+        n, drafts, qrow, prev = o["n_draft_next"], o["drafts_next"], o["q_row_next"], lg
+    seq_steps = accept_seqs * accept_steps
+    t_step = t_fwd_seq_step + t_acc / seq_steps
+    tok_per_seq_step = tokens / seq_steps
+    value = tok_per_seq_step / t_step
+    sample = (f"oracle (numpy fp64): attention + gated Q/K/V/O projections of 1 sequence at context "
+              f"{ctx_mean} for {budget_layers} of {cfg['layers']} layers (scaled to {cfg['layers']}), "
+              f"{t_fwd_seq_step:.2f} s per sequence-step; accept for {accept_seqs} sequences x "
+              f"{accept_steps} steps from FRESH at V={V}, {t_acc / seq_steps * 1e3:.1f} ms per "
+              f"sequence-step, {tok_per_seq_step:.3f} tokens per sequence-step")
+    return dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle", sample=sample)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--slices", type=int, default=0, help="attention workgroups per KV-head group (0 = automatic)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for counter scaling)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        torch.cuda.set_device(0)
+        n = 1 << 29  # 2-byte elements: 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n, "launches": 3}))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); nothing in this build runs on "
+              "several GPUs", file=sys.stderr)
+        sys.exit(2)
+
+    import draft_verify_decoding_amd as dvd
+
+    cfg = dict(CFG)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    dvd.lib()
+    K, W = args.steps, args.warmup
+    total = K + W
+    C, N, Hq, D, L, V = cfg["C"], cfg["N"], cfg["Hq"], cfg["D"], cfg["layers"], cfg["V"]
+    R = 2 * N
+
+    t_setup = time.perf_counter()
+    st = build(cfg, total, dev)
+    log(f"[bench] inputs built in {time.perf_counter() - t_setup:.1f} s")
+    logits, ctxs, nds, accs, final_ctx = dry_run(cfg, total, st["ctx0"], dev)
+    log(f"[bench] trajectory fixed: {total} steps, mean accepted {accs.mean():.3f}")
+    max_len = int(ctxs.max()) + R
+
+    # prepared calls
+    ctx = torch.from_numpy(st["ctx0"].astype(np.int32)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    att_ws = None
+    need = dvd.isd_attention_workspace_size(st["kvs"][0], C, R, Hq, max_len, args.slices)
+    if need:
+        att_ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    layer_calls = []
+    for l in range(L):
+        lay, kv = st["layers"][l], st["kvs"][l]
+        p = lay["proj"]
+        lg = lambda name, x: dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"], st["mask"],
+                                                      p[name]["y"], st["lora_ws"])
+        layer_calls.append(dict(
+            qkv=[lg("qkv", lay["x"])],
+            kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
+            att=dvd.prepare_attention(kv, lay["q"], ctx, max_len, lay["out"], ws=att_ws, slices=args.slices,
+                                      dev_err=err),
+            o=lg("o", lay["xo"])))
+    s_a, s_b = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
+    acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
+    acc_out = dvd.AcceptOutputs(C, N, R, dev, diag=False)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    att_ev = [[(ev(), ev()) for _ in range(L)] for _ in range(K)]
+    acc_ev = [(ev(), ev()) for _ in range(K)]
+
+    def step(t, timed_idx=None):
+        for l in range(L):
+            c = layer_calls[l]
+            for f in c["qkv"]:
+                f()
+            c["kvw"]()
+            if timed_idx is not None:
+                att_ev[timed_idx][l][0].record()
+            c["att"]()
+            if timed_idx is not None:
+                att_ev[timed_idx][l][1].record()
+            c["o"]()
+        s_in, s_out = (s_a, s_b) if t % 2 == 0 else (s_b, s_a)
+        if timed_idx is not None:
+            acc_ev[timed_idx][0].record()
+        dvd.isd_accept(logits[t], logits[t - 1] if t else None, s_in, s_out, N, cfg["seed"], t, out=acc_out,
+                       ws=acc_ws, ctx=ctx, dev_err=err)
+        if timed_idx is not None:
+            acc_ev[timed_idx][1].record()
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    ctx_start = ctx.cpu().numpy().copy()
+    assert np.array_equal(ctx_start, ctxs[W]), "warmup diverged from the fixed trajectory"
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, timed_idx=i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ctx_end = ctx.cpu().numpy()
+    assert err.item() == 0, f"device error flags {err.item()}"
+    assert np.array_equal(ctx_end, final_ctx), "timed run diverged from the fixed trajectory"
+    tokens = int(np.sum(ctx_end - ctx_start))  # n_emit == kv_commit per sequence-step
+
+    att_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in att_ev])  # [K, L]
+    acc_ms = np.array([a.elapsed_time(b) for a, b in acc_ev])
+    att_bytes = np.array([attention_bytes(ctxs[W + i], cfg) for i in range(K)])  # per launch, per step
+    acc_bytes = np.array([accept_bytes(nds[W + i], accs[W + i], cfg) for i in range(K)])
+    att_gbps = float(np.sum(att_bytes * L) / np.sum(att_ms) / 1e6)
+    acc_gbps = float(np.sum(acc_bytes) / np.sum(acc_ms) / 1e6)
+    aa_gbps = float((np.sum(att_bytes * L) + np.sum(acc_bytes)) / (np.sum(att_ms) + np.sum(acc_ms)) / 1e6)
+    ms_step = wall / K * 1e3
+    value = tokens / wall
+    att_only_tps = tokens / ((np.sum(att_ms) + np.sum(acc_ms)) / 1e3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "stationary batch C=64, N=4 (8-row blocks), 8B-class GQA 32/8 heads, head_dim 128, "
+                        "36 layers, bf16 paged KV (16-token pages), contexts U{1024..8192}, vocab 151936, "
+                        "acceptance ~0.9, gated-LoRA rank-32 Q/K/V/O projections; MLP and LM head not included",
+            "C": C, "N": N, "layers": L, "Hq": Hq, "Hkv": cfg["Hkv"], "head_dim": D, "vocab": V,
+            "global_batch": C, "seq_len": int(np.mean(ctxs[W])), "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "isd_attention (main + LSE merge launches of one call)",
+            "bound": "hbm",
+            "achieved": round(att_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "attention_ms_per_launch": round(float(att_ms.mean()), 5),
+        "accept_ms_per_step": round(float(acc_ms.mean()), 5),
+        "accept_gbps": round(acc_gbps, 1),
+        "attn_accept_gbps": round(aa_gbps, 1),
+        "attn_accept_frac_of_peak": round(aa_gbps / HBM_PEAK_GBPS, 4),
+        "attn_accept_only_tokens_per_s": round(float(att_only_tps), 1),
+        "tokens_per_forward": round(tokens / (K * C), 4),
+        "mean_accepted": round(float(accs[W:].mean()), 4),
+    }
+    if not args.no_cpu_baseline:
+        t_cpu = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline(cfg)
+        log(f"[bench] cpu baseline took {time.perf_counter() - t_cpu:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,6 +62,7 @@ class IsdAcceptArgs(ctypes.Structure):
         ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64),
         ("accepted", ctypes.c_void_p), ("n_emit", ctypes.c_void_p),
         ("emit", ctypes.c_void_p), ("kv_commit", ctypes.c_void_p),
+        ("ctx", ctypes.c_void_p),
         ("p_x", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p),
         ("row_m", ctypes.c_void_p), ("row_s", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
@@ -171,24 +172,24 @@ def isd_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
     _check(rc, "isd_kv_write")
 
 
-def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, chunk=0):
+def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, slices=0):
     s = kv.c_struct()
-    return int(lib().isd_attention_workspace_size(C, rows, num_q_heads, ctypes.byref(s), max_len, chunk))
+    return int(lib().isd_attention_workspace_size(C, rows, num_q_heads, ctypes.byref(s), max_len, slices))
 
 
-def isd_attention(kv, q, ctx, max_len, scale=None, chunk=0, out=None, ws=None, dev_err=None, stream=None):
+def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, dev_err=None, stream=None):
     """out [C, rows, Hq, D] fp32 = causal attention of q over the pages."""
     C, rows, Hq, D = q.shape
     if scale is None:
         scale = D ** -0.5
     if out is None:
         out = torch.empty((C, rows, Hq, D), dtype=torch.float32, device=q.device)
-    need = isd_attention_workspace_size(kv, C, rows, Hq, max_len, chunk)
+    need = isd_attention_workspace_size(kv, C, rows, Hq, max_len, slices)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     s = kv.c_struct()
     rc = lib().isd_attention(ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
-                             int(chunk), _p(out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                             int(slices), _p(out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                              _p(dev_err), _stream(stream))
     _check(rc, "isd_attention")
     return out
@@ -237,9 +238,10 @@ class AcceptOutputs:
 
 
 def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
-               diag=False, dev_err=None, stream=None):
+               diag=False, dev_err=None, ctx=None, stream=None):
     """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
-    AcceptOutputs (device tensors) and writes state_out."""
+    AcceptOutputs (device tensors) and writes state_out. If ctx (int32 [C])
+    is given, the kernel adds kv_commit to it."""
     C, rows, ld = logits.shape
     V = ld if V is None else V
     if out is None:
@@ -258,6 +260,7 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     args.seed, args.step = int(seed), int(step)
     args.accepted, args.n_emit = out.accepted.data_ptr(), out.n_emit.data_ptr()
     args.emit, args.kv_commit = out.emit.data_ptr(), out.kv_commit.data_ptr()
+    args.ctx = None if ctx is None else ctx.data_ptr()
     for name in ("p_x", "resid_mass", "row_m", "row_s"):
         t = getattr(out, name)
         setattr(args, name, None if t is None else t.data_ptr())
@@ -304,3 +307,44 @@ def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=Non
                                 _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "isd_linear_gated")
     return y
+
+
+# ------------------------------------------------------- prepared calls
+class Prepared:
+    """One library call with its arguments marshalled once, for loops that
+    issue the same call many times (the arguments' tensors must stay alive
+    and in place). Calling it runs the call and raises on an error code."""
+
+    def __init__(self, name, *args, keep=()):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise IsdError(rc, self.name)
+
+
+def prepare_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
+    s = kv.c_struct()
+    return Prepared("isd_kv_write", ctypes.byref(s), _p(k), _p(v), _p(pos0), _p(nrows), k.shape[0], k.shape[1],
+                    _p(dev_err), _stream(stream), keep=(s, kv, k, v, pos0, nrows, dev_err))
+
+
+def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, dev_err=None, stream=None):
+    C, rows, Hq, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    s = kv.c_struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return Prepared("isd_attention", ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
+                    int(slices), _p(out), _p(ws), nbytes, _p(dev_err), _stream(stream),
+                    keep=(s, kv, q, ctx, out, ws, dev_err))
+
+
+def prepare_linear_gated(x, W, A, B, is_mask, y, ws, scale=1.0, stream=None):
+    M, K = x.shape
+    return Prepared("isd_linear_gated", _p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, W.shape[0], A.shape[0],
+                    float(scale), _p(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream),
+                    keep=(x, W, A, B, is_mask, y, ws))

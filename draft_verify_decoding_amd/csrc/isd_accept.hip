@@ -38,7 +38,7 @@ struct AcceptParams {
   int C, N, V, rows, nch, ns;
   isd_seq_state in, out;
   uint64_t seed, step;
-  int32_t *accepted, *n_emit, *emit, *kv_commit;
+  int32_t *accepted, *n_emit, *emit, *kv_commit, *ctx;
   float *p_x, *resid_mass, *row_m, *row_s;
   float2* stats;    // [C][rows][nch] (chunk max, chunk sum)
   float* resid;     // [C][ns] residual slice sums
@@ -472,6 +472,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
     p.accepted[b] = a;
     p.n_emit[b] = a + 1;
     p.kv_commit[b] = a + 1;
+    if (p.ctx) p.ctx[b] += a + 1;
     for (int k = 0; k < N; ++k) {
       int v = -1;
       if (k < a) v = p.in.drafts[b * nd + k];
@@ -594,6 +595,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.n_emit = a->n_emit;
   p.emit = a->emit;
   p.kv_commit = a->kv_commit;
+  p.ctx = a->ctx;
   p.p_x = a->p_x;
   p.resid_mass = a->resid_mass;
   p.row_m = a->row_m;

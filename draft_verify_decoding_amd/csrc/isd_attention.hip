@@ -20,13 +20,17 @@
 //    lane, so the rescale by exp2(m_old - m_new) is a per-lane multiply.
 //  * P is split into bf16 hi + lo halves (two MFMAs), keeping about 16
 //    mantissa bits on the softmax weights.
-//  * Page layout (isd.h) makes every operand a run of 16 contiguous bytes:
-//    K [Hkv][D/8][16 slots][8], V [Hkv][D][16 slots].
+//  * Page layout (isd.h) makes every operand a run of 16 contiguous bytes
+//    and every 4-lane group a run of 64: K [Hkv][D/8][16 slots][8],
+//    V [Hkv][2 half-pages][D][8 slots].
 //  * Split-KV: a workgroup of 4 waves reduces one chunk of one (sequence,
 //    KV head); waves interleave 32-key tiles and merge through LDS; units
 //    with several chunks write (m, l, O) partials that a second kernel merges
 //    in chunk order, so results do not depend on scheduling.
 #include "isd_common.hpp"
+
+#include <algorithm>
+#include <climits>
 
 namespace isd {
 
@@ -37,12 +41,14 @@ struct AttnParams {
   const void* q;
   const int32_t* ctx;
   float* out;
-  float* part_o;   // [units][max_chunks][MB*32][D]
-  float* part_ml;  // [units][max_chunks][MB*32][2]
+  float* part_o;    // [groups * G][2 slots][HPW * MB][32][D]
+  float* part_ml;   // same, [2]: (max, sum)
+  int32_t* tile_off;  // [C + 1] tile offsets written for the merge launch
   int32_t* dev_err;
   int table_stride, num_pages;
   int C, rows, Hq, Hkv, group, M;
-  int chunk, max_chunks;
+  int G;             // slices (workgroups) per KV-head group
+  int MB, HPW;       // query blocks and KV heads per workgroup (one wave each)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -73,6 +79,11 @@ struct AttnOps<uint16_t> {
     u32x4 v = *reinterpret_cast<const u32x4*>(p);
     return __builtin_bit_cast(bf16x8, v);
   }
+  // K/V stream through once: non-temporal loads keep them out of the way in
+  // the caches (measured about 7% faster than plain loads on this kernel).
+  static __device__ __forceinline__ bf16x8 load16_stream(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  }
   static __device__ __forceinline__ bf16x8 zero() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
 
   template <int D>
@@ -86,16 +97,18 @@ struct AttnOps<uint16_t> {
   static __device__ __forceinline__ void load_k(Regs<D>& r, const uint16_t* kpage, bool valid, int slot, int hh) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      r.k[s] = valid ? load16(kpage + ((2 * s + hh) * 16 + slot) * 8) : zero();
+      r.k[s] = valid ? load16_stream(kpage + ((2 * s + hh) * 16 + slot) * 8) : zero();
   }
   // V^T operand: lane (dim d, half hh) at k-step p (= tile page p) holds
-  // slots 8hh .. 8hh+7 of dim d. Keys at or past `limit` are zeroed.
+  // slots 8hh .. 8hh+7 of dim d, which the page stores as 16 contiguous
+  // bytes right after those of dim d-1 (layout [2][D][8]): every group of
+  // four lanes reads 64 contiguous bytes. Keys at or past `limit` are zeroed.
   template <int D>
   static __device__ __forceinline__ void load_v(Regs<D>& r, const uint16_t* vpage, int p, bool valid, int lane32,
                                                 int hh, int first_key, int limit) {
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) {
-      bf16x8 v = valid ? load16(vpage + (nb * 32 + lane32) * 16 + 8 * hh) : zero();
+      bf16x8 v = valid ? load16_stream(vpage + (hh * D + nb * 32 + lane32) * 8) : zero();
       if (first_key + 8 > limit) {
         u32x4 w = __builtin_bit_cast(u32x4, v);
 #pragma unroll
@@ -174,7 +187,7 @@ struct AttnOps<float> {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         bool ok = valid && (first_key + k < limit);
-        r.v[nb][8 * p + k] = ok ? vpage[(nb * 32 + lane32) * 16 + 8 * hh + k] : 0.f;
+        r.v[nb][8 * p + k] = ok ? vpage[(hh * D + nb * 32 + lane32) * 8 + k] : 0.f;
       }
   }
   template <int D>
@@ -193,219 +206,338 @@ struct AttnOps<float> {
   }
 };
 
+constexpr int kMaxSeqs = 8192;   // sequences per attention call (LDS prefix sums)
+constexpr int kTileBatch = 1024;  // tiles whose page ids are staged in LDS at once
+
 template <typename E, int D>
 __device__ __forceinline__ const E* page_ptr(const void* pool, int pid, int Hkv, int g) {
   return static_cast<const E*>(pool) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
 }
 
-// One workgroup = 4 waves = one (chunk, sequence, KV head). Wave w handles
-// query block rb = w % MB and interleaved tile stream ts = w / MB.
-template <typename E, int D, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
+// Work split ("stream-K"): the tiles (32 keys) of all sequences are laid
+// end to end, tiles(b) = ceil((ctx_b + rows) / 32), and slice w of G takes
+// tiles [floor(w*T/G), floor((w+1)*T/G)) of that list, so every workgroup
+// streams the same number of bytes however ragged the contexts are. A
+// workgroup holds HPW KV heads x MB query blocks, one wave each; its waves
+// walk the same pages together (all heads of a page are contiguous). A
+// sequence that lies wholly inside one slice is finalised in registers; the
+// pieces of a sequence shared by several slices are written to two partial
+// slots per slice (its first and its last sequence) and merged afterwards in
+// slice order, so results do not depend on scheduling.
+template <typename E, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   using Ops = AttnOps<E>;
-  constexpr int SW = 4 / MB;  // tile streams per query block
-  const int units = p.C * p.Hkv;
-  const int unit = blockIdx.x % units;
-  const int chunk = blockIdx.x / units;
-  const int b = unit / p.Hkv;
-  const int g = unit % p.Hkv;
-  const int ctx = p.ctx[b];
-  const int L = ctx + p.rows;  // positions 0 .. L-1 are read
-  const int c0 = chunk * p.chunk;
-  if (ctx < 0) {
-    if (chunk == 0 && threadIdx.x == 0) set_dev_err(p.dev_err, ISD_DEV_STATE);
-    return;
+  const int MB = p.MB;
+  const int G = p.G;
+  const int hg = blockIdx.x / G;
+  const int w = blockIdx.x % G;
+  const int nthreads = 64 * p.HPW * MB;
+
+  // Tile offsets of the sequences (prefix sum), rebuilt by every workgroup.
+  __shared__ int s_off[kMaxSeqs + 1];
+  __shared__ int s_part[512];
+  __shared__ int s_pid[2 * kTileBatch];  // page ids of the current tile batch
+  {
+    const int per = (p.C + nthreads - 1) / nthreads;
+    const int b0 = threadIdx.x * per;
+    int sum = 0;
+    for (int b = b0; b < min(p.C, b0 + per); ++b) {
+      const int ctx = p.ctx[b];
+      sum += ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
+    }
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int run = 0;
+      for (int t = 0; t < nthreads; ++t) {
+        const int v = s_part[t];
+        s_part[t] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    int run = s_part[threadIdx.x];
+    for (int b = b0; b < min(p.C, b0 + per); ++b) {
+      s_off[b] = run;
+      const int ctx = p.ctx[b];
+      if (ctx < 0 && w == 0 && hg == 0) set_dev_err(p.dev_err, ISD_DEV_STATE);
+      run += ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
+    }
+    if (b0 < p.C && min(p.C, b0 + per) == p.C) s_off[p.C] = run;
+    __syncthreads();
   }
-  const int nchunks = (L + p.chunk - 1) / p.chunk;
-  if (nchunks > p.max_chunks) {  // ctx + rows exceeds the max_len the grid was sized for
-    if (chunk == 0 && threadIdx.x == 0) set_dev_err(p.dev_err, ISD_DEV_CAPACITY);
-    return;
+  const long T = s_off[p.C];
+  const int t_begin = static_cast<int>(w * T / G);
+  const int t_end = static_cast<int>((w + 1) * T / G);
+  if (w == 0 && hg == 0)  // the merge launch reads the offsets back
+    for (int b = threadIdx.x; b <= p.C; b += nthreads) p.tile_off[b] = s_off[b];
+  if (t_begin >= t_end) return;
+  int u_first = 0;  // sequence holding tile t_begin
+  {
+    int lo = 0, hi = p.C - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (s_off[mid] <= t_begin) lo = mid; else hi = mid - 1;
+    }
+    u_first = lo;
   }
-  if (c0 >= L) return;
-  const int c1 = min(L, c0 + p.chunk);
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int lane32 = lane & 31;
   const int hh = lane >> 5;
   const int rb = wave % MB;
-  const int ts = wave / MB;
-
-  // Query column of this lane.
-  const int qi = rb * 32 + lane32;
+  const int hl_w = wave / MB;
+  const int g = hg * p.HPW + hl_w;
+  const int qi = rb * 32 + lane32;  // query column of this lane
   const bool qvalid = qi < p.M;
   const int hl = qvalid ? qi / p.rows : 0;
   const int irow = qvalid ? qi % p.rows : p.rows - 1;
   const int h = g * p.group + hl;
-  const int vis_limit = ctx + irow;  // last visible position
-
-  typename Ops::template Regs<D> r;
-  const E* qrow = static_cast<const E*>(p.q) + ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
-  Ops::template load_q<D>(r, qrow, qvalid, hh);
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) o[nb] = f32x16{};
-  float m_run = -1e30f;  // finite floor: exp2(m_old - m_new) stays defined
-  float l_run = 0.f;
-
-  const int32_t* table = p.block_table + static_cast<size_t>(b) * p.table_stride;
   const int krow_key = tile_key_of_row(lane32);  // tile key this lane loads for K
+  const int kpg = krow_key >> 4;
+  const int kslot = krow_key & 15;
   uint32_t err = 0;
 
-  for (int t0 = c0 + 32 * ts; t0 < c1; t0 += 32 * SW) {
-    // Resolve the tile's two pages.
-    const E* kp[2];
-    const E* vp[2];
-    bool pv_ok[2];
+  typename Ops::template Regs<D> r;
+  f32x16 o[D / 32];
+  float m_run, l_run;
+
+  for (int b = u_first; b < p.C && s_off[b] < t_end; ++b) {
+    const int tb0 = s_off[b], tb1 = s_off[b + 1];
+    const int lt0 = max(t_begin, tb0) - tb0, lt1 = min(t_end, tb1) - tb0;
+    if (lt0 >= lt1) continue;
+    const int ctx = p.ctx[b];
+    const int L = ctx + p.rows;  // positions 0 .. L-1 are read
+    const int vis_limit = ctx + irow;
+    const int32_t* table = p.block_table + static_cast<size_t>(b) * p.table_stride;
+
+    const E* qrow = static_cast<const E*>(p.q) + ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
+    Ops::template load_q<D>(r, qrow, qvalid, hh);
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const int first = t0 + 16 * pg;
-      bool ok = first < L;
-      int pid = 0;
-      if (ok) {
-        const int col = first >> 4;
-        if (col >= p.table_stride) {
-          err |= ISD_DEV_CAPACITY;
-          ok = false;
-        } else {
-          pid = table[col];
-          if (pid < 0 || pid >= p.num_pages) {
-            err |= ISD_DEV_PAGE_OOB;
-            ok = false;
-          }
+    for (int nb = 0; nb < D / 32; ++nb) o[nb] = f32x16{};
+    m_run = -1e30f;  // finite floor: exp2(m_old - m_new) stays defined
+    l_run = 0.f;
+
+    auto clamp_pid = [&](int pid) {
+      if (pid < 0 || pid >= p.num_pages) {
+        err |= ISD_DEV_PAGE_OOB;
+        return 0;
+      }
+      return pid;
+    };
+    // online-softmax update and PV product for one tile of scores
+    auto consume = [&](const f32x16& s, int t0, bool masked) {
+      float sv[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[e];
+        if (masked) x = (t0 + tile_key_of_reg(e, hh) <= vis_limit) ? x : -INFINITY;
+        sv[e] = x;
+        tmax = fmaxf(tmax, x);
+      }
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax * p.scale_log2);
+      float pr[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pr[e] = fast_exp2(fmaf(sv[e], p.scale_log2, -m_new));
+        psum += pr[e];
+      }
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {  // some row maximum grew
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
+      }
+      m_run = m_new;
+      l_run += psum;
+      Ops::template pv<D>(r, pr, o);
+    };
+
+    // The piece's page ids are staged in LDS a batch at a time (one
+    // cooperative load), so no tile waits on a block-table round trip
+    // before it can issue its K/V loads.
+    const int full_end = min(lt1, max(0, min(ctx + 1, p.table_stride * 16) / 32));
+    for (int bt0 = lt0; bt0 < lt1; bt0 += kTileBatch) {
+      const int bt1 = min(lt1, bt0 + kTileBatch);
+      __syncthreads();  // the previous batch is no longer read
+      for (int i = threadIdx.x; i < 2 * (bt1 - bt0); i += nthreads) {
+        const int col = 2 * bt0 + i;
+        s_pid[i] = col < p.table_stride ? table[col] : -1;
+      }
+      __syncthreads();
+
+      // Full tiles (all 32 keys visible to every row, pages inside the
+      // table) run a straight-line, software-pipelined loop: the K loads of
+      // the next tile are issued as soon as QK^T has consumed the K
+      // registers, the V loads right after PV.
+      const int fe = min(bt1, full_end);
+      int lt = bt0;
+      if (lt < fe) {
+        const E* kpage;
+        const E* vpage0;
+        const E* vpage1;
+        auto pages = [&](int tl) {
+          const int pid0 = clamp_pid(s_pid[2 * (tl - bt0)]), pid1 = clamp_pid(s_pid[2 * (tl - bt0) + 1]);
+          kpage = page_ptr<E, D>(p.k_pages, kpg ? pid1 : pid0, p.Hkv, g);
+          vpage0 = page_ptr<E, D>(p.v_pages, pid0, p.Hkv, g);
+          vpage1 = page_ptr<E, D>(p.v_pages, pid1, p.Hkv, g);
+        };
+        pages(lt);
+        Ops::template load_k<D>(r, kpage, true, kslot, hh);
+        Ops::template load_v<D>(r, vpage0, 0, true, lane32, hh, 0, INT_MAX);
+        Ops::template load_v<D>(r, vpage1, 1, true, lane32, hh, 0, INT_MAX);
+        for (;;) {
+          const bool more = lt + 1 < fe;
+          pages(more ? lt + 1 : lt);  // past the end: reload this tile, unused
+          const f32x16 sc = Ops::template qk<D>(r);
+          Ops::template load_k<D>(r, kpage, true, kslot, hh);
+          // Keep the prefetches where they are: without these barriers the
+          // compiler sinks them next to their use and the load latency is
+          // exposed on every tile.
+          asm volatile("" ::: "memory");
+          consume(sc, 32 * lt, false);
+          Ops::template load_v<D>(r, vpage0, 0, true, lane32, hh, 0, INT_MAX);
+          Ops::template load_v<D>(r, vpage1, 1, true, lane32, hh, 0, INT_MAX);
+          asm volatile("" ::: "memory");
+          ++lt;
+          if (!more) break;
         }
       }
-      pv_ok[pg] = ok;
-      kp[pg] = page_ptr<E, D>(p.k_pages, ok ? pid : 0, p.Hkv, g);
-      vp[pg] = page_ptr<E, D>(p.v_pages, ok ? pid : 0, p.Hkv, g);
-    }
-    {
-      const int kpg = krow_key >> 4;
-      Ops::template load_k<D>(r, kpg ? kp[1] : kp[0], pv_ok[kpg], krow_key & 15, hh);
-    }
+      for (; lt < bt1; ++lt) {  // boundary tiles: causal mask, positions past L, table end
+        const int t0 = 32 * lt;
+        const E* kp[2];
+        const E* vp[2];
+        bool ok[2];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-      Ops::template load_v<D>(r, vp[pg], pg, pv_ok[pg], lane32, hh, t0 + 16 * pg + 8 * hh, L);
-
-    f32x16 s = Ops::template qk<D>(r);
-
-    float sv[16];
-    float tmax = -INFINITY;
-    const bool need_mask = t0 + 31 > ctx;
+        for (int pg = 0; pg < 2; ++pg) {
+          const int first = t0 + 16 * pg;
+          bool valid = first < L;
+          int pid = 0;
+          if (valid) {
+            if ((first >> 4) >= p.table_stride) {
+              err |= ISD_DEV_CAPACITY;
+              valid = false;
+            } else {
+              pid = s_pid[2 * (lt - bt0) + pg];
+              if (pid < 0 || pid >= p.num_pages) {
+                err |= ISD_DEV_PAGE_OOB;
+                valid = false;
+                pid = 0;
+              }
+            }
+          }
+          ok[pg] = valid;
+          kp[pg] = page_ptr<E, D>(p.k_pages, pid, p.Hkv, g);
+          vp[pg] = page_ptr<E, D>(p.v_pages, pid, p.Hkv, g);
+        }
+        Ops::template load_k<D>(r, kpg ? kp[1] : kp[0], kpg ? ok[1] : ok[0], kslot, hh);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = s[e];
-      if (need_mask) {
-        const int key = t0 + tile_key_of_reg(e, hh);
-        x = (key <= vis_limit) ? x : -INFINITY;
+        for (int pg = 0; pg < 2; ++pg)
+          Ops::template load_v<D>(r, vp[pg], pg, ok[pg], lane32, hh, t0 + 16 * pg + 8 * hh, L);
+        consume(Ops::template qk<D>(r), t0, true);
       }
-      sv[e] = x;
-      tmax = fmaxf(tmax, x);
     }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax * p.scale_log2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float pr[16];
-    float psum = 0.f;
+
+    // Finalise this (sequence, head, query block) piece. Register e of
+    // block nb holds dim 32nb + 8(e/4) + 4hh + e%4: four registers make one
+    // 16-byte store.
+    const float l_tot = l_run + shfl_xor_f(l_run, 32);
+    const bool whole = lt0 == 0 && lt1 == tb1 - tb0;
+    if (qvalid) {
+      float* dst;
+      float mul;
+      if (whole) {
+        dst = p.out + ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
+        mul = 1.f / l_tot;
+      } else {
+        const int slot = (b == u_first) ? 0 : 1;
+        const size_t idx = ((static_cast<size_t>(hg * G + w) * 2 + slot) * (p.HPW * MB) + hl_w * MB + rb) * 32 + lane32;
+        dst = p.part_o + idx * D;
+        mul = 1.f;
+        if (hh == 0) {
+          p.part_ml[idx * 2] = m_run;
+          p.part_ml[idx * 2 + 1] = l_tot;
+        }
+      }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pr[e] = fast_exp2(fmaf(sv[e], p.scale_log2, -m_new));
-      psum += pr[e];
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[nb][4 * q4 + e] * mul;
+          *reinterpret_cast<f32x4*>(dst + nb * 32 + 8 * q4 + 4 * hh) = v;
+        }
     }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
-    Ops::template pv<D>(r, pr, o);
   }
   if (err) set_dev_err(p.dev_err, err);
-
-  // Lane-half partial sums -> per-column totals.
-  l_run += shfl_xor_f(l_run, 32);
-
-  // Merge the SW tile streams of each query block through LDS.
-  __shared__ float s_o[4][D][33];
-  __shared__ float s_m[4][32];
-  __shared__ float s_l[4][32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d = nb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-      s_o[wave][d][lane32] = o[nb][e];
-    }
-  if (hh == 0) {
-    s_m[wave][lane32] = m_run;
-    s_l[wave][lane32] = l_run;
-  }
-  __syncthreads();
-
-  const bool final_out = nchunks == 1;
-  for (int idx = threadIdx.x; idx < MB * 32 * D; idx += 256) {
-    const int d = idx % D;
-    const int j = (idx / D) % 32;
-    const int qb = idx / (32 * D);
-    const int col = qb * 32 + j;
-    if (col >= p.M) continue;
-    float mstar = -1e30f;
-#pragma unroll
-    for (int st = 0; st < SW; ++st) mstar = fmaxf(mstar, s_m[qb + MB * st][j]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int st = 0; st < SW; ++st) {
-      const int w = qb + MB * st;
-      const float wt = fast_exp2(s_m[w][j] - mstar);
-      acc = fmaf(wt, s_o[w][d][j], acc);
-      lsum = fmaf(wt, s_l[w][j], lsum);
-    }
-    if (final_out) {
-      const int hl2 = col / p.rows, i2 = col % p.rows;
-      const int h2 = g * p.group + hl2;
-      p.out[((static_cast<size_t>(b) * p.rows + i2) * p.Hq + h2) * D + d] = acc / lsum;
-    } else {
-      const size_t base = (static_cast<size_t>(unit) * p.max_chunks + chunk) * (MB * 32) + col;
-      p.part_o[base * D + d] = acc;
-      if (d == 0) {
-        p.part_ml[base * 2] = mstar;
-        p.part_ml[base * 2 + 1] = lsum;
-      }
-    }
-  }
 }
 
-// Log-sum-exp merge of the chunk partials of one (sequence, KV head) in
-// chunk order. One workgroup per unit and query block.
-template <int D, int MB>
+// Log-sum-exp merge of the pieces of one (sequence, KV head, query block)
+// held by several slices, in slice order. Thread t owns query column t/8
+// and D/8 consecutive dims, read and written as float4.
+template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
-  const int unit = blockIdx.x;
+  const int MB = p.MB;
+  const int b = blockIdx.x / p.Hkv;
+  const int g = blockIdx.x % p.Hkv;
   const int qb = blockIdx.y;
-  const int b = unit / p.Hkv;
-  const int g = unit % p.Hkv;
-  const int ctx = p.ctx[b];
-  if (ctx < 0) return;
-  const int L = ctx + p.rows;
-  const int nchunks = (L + p.chunk - 1) / p.chunk;
-  if (nchunks <= 1 || nchunks > p.max_chunks) return;
-  for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
-    const int d = idx % D;
-    const int col = qb * 32 + idx / D;
-    if (col >= p.M) continue;
-    const size_t base0 = static_cast<size_t>(unit) * p.max_chunks * (MB * 32) + col;
-    float mstar = -1e30f;
-    for (int c = 0; c < nchunks; ++c) mstar = fmaxf(mstar, p.part_ml[(base0 + c * (MB * 32)) * 2]);
-    float acc = 0.f, lsum = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const size_t base = base0 + static_cast<size_t>(c) * (MB * 32);
-      const float wt = fast_exp2(p.part_ml[base * 2] - mstar);
-      acc = fmaf(wt, p.part_o[base * D + d], acc);
-      lsum = fmaf(wt, p.part_ml[base * 2 + 1], lsum);
+  const int G = p.G;
+  const int hg = g / p.HPW, hl_w = g % p.HPW;
+  const long T = p.tile_off[p.C];
+  const int tb0 = p.tile_off[b], tb1 = p.tile_off[b + 1];
+  if (tb1 <= tb0 || T == 0) return;
+  // slice holding tile x: the largest w with floor(w*T/G) <= x
+  auto slice_of = [&](long x) { return static_cast<int>(((x + 1) * G + T - 1) / T - 1); };
+  const int wa = slice_of(tb0), wb = slice_of(tb1 - 1);
+  if (wa == wb) return;  // finalised by its slice
+  constexpr int kDimsPerThread = D * 32 / 256;
+  const int col = qb * 32 + threadIdx.x / (256 / 32);
+  const int d0 = (threadIdx.x % (256 / 32)) * kDimsPerThread;
+  if (col >= p.M) return;
+  auto piece = [&](int w2) {
+    const long start = w2 * T / G;
+    const int slot = start >= tb0 ? 0 : 1;
+    return ((static_cast<size_t>(hg * G + w2) * 2 + slot) * (p.HPW * MB) + hl_w * MB + qb) * 32 + (col - qb * 32);
+  };
+  // a slice whose range is empty (more slices than tiles) holds no piece
+  auto empty = [&](int w2) { return (w2 * T / G) == ((w2 + 1) * T / G); };
+  float mstar = -1e30f;
+  for (int w2 = wa; w2 <= wb; ++w2)
+    if (!empty(w2)) mstar = fmaxf(mstar, p.part_ml[piece(w2) * 2]);
+  f32x4 acc[kDimsPerThread / 4];
+#pragma unroll
+  for (int k = 0; k < kDimsPerThread / 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  for (int w2 = wa; w2 <= wb; ++w2) {
+    if (empty(w2)) continue;
+    const size_t idx = piece(w2);
+    const float wt = fast_exp2(p.part_ml[idx * 2] - mstar);
+    lsum = fmaf(wt, p.part_ml[idx * 2 + 1], lsum);
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
+#pragma unroll
+    for (int k = 0; k < kDimsPerThread / 4; ++k) {
+      const f32x4 v = src[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(wt, v[e], acc[k][e]);
     }
-    const int hl = col / p.rows, i = col % p.rows;
-    const int h = g * p.group + hl;
-    p.out[((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d] = acc / lsum;
+  }
+  const int hl = col / p.rows, i = col % p.rows;
+  const int h = g * p.group + hl;
+  f32x4* dst = reinterpret_cast<f32x4*>(p.out + ((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d0);
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int k = 0; k < kDimsPerThread / 4; ++k) {
+    f32x4 v = acc[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = v[e] * inv;
+    dst[k] = v;
   }
 }
 
@@ -448,7 +580,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(void* k_pages, void* v_pa
   *reinterpret_cast<u32x4*>(kpage + (c * 16 + slot) * KP) = kv;
   const E* ve = reinterpret_cast<const E*>(&vv);
 #pragma unroll
-  for (int j = 0; j < KP; ++j) vpage[(c * KP + j) * 16 + slot] = ve[j];
+  for (int j = 0; j < KP; ++j) vpage[((slot >> 3) * D + c * KP + j) * 8 + (slot & 7)] = ve[j];
 }
 
 }  // namespace isd
@@ -471,59 +603,47 @@ int check_kv(const isd_kv_cache* kv) {
   return ISD_OK;
 }
 
-int auto_chunk(int units, int max_len) {
-  // Aim at about 1024 workgroups of 4 waves, tiles of 32 keys.
-  long want = (static_cast<long>(units) * max_len + 1023) / 1024;
-  long c = ((want + 31) / 32) * 32;
-  if (c < 64) c = 64;
-  if (c > 4096) c = 4096;
-  return static_cast<int>(c);
-}
-
 struct AttnPlan {
-  int chunk, max_chunks, MB;
-  size_t part_o_bytes, part_ml_bytes;
+  int MB, HPW, groups, G;
+  size_t off_bytes, part_o_bytes, part_ml_bytes;
+  size_t total() const { return off_bytes + part_o_bytes + part_ml_bytes; }
 };
 
-int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len, int chunk, AttnPlan* plan) {
+int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len, int slices, AttnPlan* plan) {
   if (C < 0 || rows < 1 || rows > 64 || Hq < 1) return ISD_E_INVALID;
+  if (C > kMaxSeqs) return ISD_E_UNSUPPORTED;
   const int Hkv = kv->num_kv_heads;
   if (Hq % Hkv != 0) return ISD_E_UNSUPPORTED;
   const int M = (Hq / Hkv) * rows;
   if (M > 128) return ISD_E_UNSUPPORTED;
   if (max_len < rows) return ISD_E_INVALID;
-  if (chunk < 0 || chunk % 32 != 0) return ISD_E_INVALID;
+  if (slices < 0) return ISD_E_INVALID;
   plan->MB = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
-  plan->chunk = chunk ? chunk : auto_chunk(C * Hkv, max_len);
-  plan->max_chunks = (max_len + plan->chunk - 1) / plan->chunk;
-  const size_t cols = static_cast<size_t>(C) * Hkv * plan->max_chunks * plan->MB * 32;
-  if (plan->max_chunks > 1) {
-    plan->part_o_bytes = cols * kv->head_dim * sizeof(float);
-    plan->part_ml_bytes = cols * 2 * sizeof(float);
-  } else {
-    plan->part_o_bytes = plan->part_ml_bytes = 0;
-  }
+  // KV heads per workgroup: the largest power of two that divides Hkv with
+  // at most 8 waves (one per head and query block) in the workgroup.
+  plan->HPW = 1;
+  while (plan->HPW * 2 * plan->MB <= 8 && Hkv % (plan->HPW * 2) == 0) plan->HPW *= 2;
+  plan->groups = Hkv / plan->HPW;
+  // Default: 2048 waves over the chip (8 per CU: the register-file limit of
+  // this kernel), spread over the head groups; never more slices than tiles.
+  long G = slices ? slices : std::max(1, 2048 / (plan->HPW * plan->MB) / plan->groups);
+  const long max_tiles = static_cast<long>(C) * ((max_len + 31) / 32);
+  if (G > max_tiles) G = std::max(1L, max_tiles);
+  plan->G = static_cast<int>(G);
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t pieces = static_cast<size_t>(plan->groups) * plan->G * 2 * plan->HPW * plan->MB * 32;
+  plan->off_bytes = up(static_cast<size_t>(C + 1) * sizeof(int32_t));
+  plan->part_o_bytes = up(pieces * kv->head_dim * sizeof(float));
+  plan->part_ml_bytes = up(pieces * 2 * sizeof(float));
   return ISD_OK;
 }
 
 template <typename E, int D>
-hipError_t launch_attention_typed(const AttnParams& p, int MB, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.C * p.Hkv * p.max_chunks));
-  const dim3 mgrid(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(MB));
-  switch (MB) {
-    case 1:
-      hipLaunchKernelGGL((attention_kernel<E, D, 1>), grid, dim3(256), 0, stream, p);
-      if (p.max_chunks > 1) hipLaunchKernelGGL((attention_merge_kernel<D, 1>), mgrid, dim3(256), 0, stream, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((attention_kernel<E, D, 2>), grid, dim3(256), 0, stream, p);
-      if (p.max_chunks > 1) hipLaunchKernelGGL((attention_merge_kernel<D, 2>), mgrid, dim3(256), 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((attention_kernel<E, D, 4>), grid, dim3(256), 0, stream, p);
-      if (p.max_chunks > 1) hipLaunchKernelGGL((attention_merge_kernel<D, 4>), mgrid, dim3(256), 0, stream, p);
-      break;
-  }
+hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t stream) {
+  hipLaunchKernelGGL((attention_kernel<E, D>), dim3(static_cast<unsigned>(groups * p.G)),
+                     dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
+  hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(p.MB)),
+                     dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -532,15 +652,15 @@ hipError_t launch_attention_typed(const AttnParams& p, int MB, hipStream_t strea
 extern "C" {
 
 size_t isd_attention_workspace_size(int C, int rows, int num_q_heads, const isd_kv_cache* kv, int max_len,
-                                    int chunk) {
+                                    int slices) {
   if (!kv || kv->num_kv_heads < 1 || (kv->head_dim != 64 && kv->head_dim != 128)) return 0;
   AttnPlan plan;
-  if (plan_attention(C, rows, num_q_heads, kv, max_len, chunk, &plan) != ISD_OK) return 0;
-  return plan.part_o_bytes + plan.part_ml_bytes;
+  if (plan_attention(C, rows, num_q_heads, kv, max_len, slices, &plan) != ISD_OK) return 0;
+  return plan.total();
 }
 
 int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int C, int rows, int num_q_heads,
-                  float scale, int max_len, int chunk, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
+                  float scale, int max_len, int slices, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
                   hipStream_t stream) {
   int rc = check_kv(kv);
   if (rc) return rc;
@@ -549,10 +669,9 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   if (!(scale > 0.f) || !(scale < INFINITY)) return ISD_E_INVALID;
   if (!aligned16(q) || !aligned16(out)) return ISD_E_INVALID;
   AttnPlan plan;
-  rc = plan_attention(C, rows, num_q_heads, kv, max_len, chunk, &plan);
+  rc = plan_attention(C, rows, num_q_heads, kv, max_len, slices, &plan);
   if (rc) return rc;
-  const size_t need = plan.part_o_bytes + plan.part_ml_bytes;
-  if (need && (!ws || ws_bytes < need || !aligned16(ws))) return ISD_E_WORKSPACE;
+  if (!ws || ws_bytes < plan.total() || !aligned16(ws)) return ISD_E_WORKSPACE;
   rc = isd_check_device_internal();
   if (rc) return rc;
 
@@ -563,8 +682,10 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   p.q = q;
   p.ctx = ctx;
   p.out = out;
-  p.part_o = need ? static_cast<float*>(ws) : nullptr;
-  p.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_o_bytes) : nullptr;
+  char* w = static_cast<char*>(ws);
+  p.tile_off = reinterpret_cast<int32_t*>(w);
+  p.part_o = reinterpret_cast<float*>(w + plan.off_bytes);
+  p.part_ml = reinterpret_cast<float*>(w + plan.off_bytes + plan.part_o_bytes);
   p.dev_err = dev_err;
   p.table_stride = kv->table_stride;
   p.num_pages = kv->num_pages;
@@ -574,17 +695,18 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   p.Hkv = kv->num_kv_heads;
   p.group = num_q_heads / kv->num_kv_heads;
   p.M = p.group * rows;
-  p.chunk = plan.chunk;
-  p.max_chunks = plan.max_chunks;
+  p.G = plan.G;
+  p.MB = plan.MB;
+  p.HPW = plan.HPW;
   p.scale_log2 = scale * kLog2e;
 
   hipError_t e;
   if (kv->dtype == ISD_BF16)
-    e = kv->head_dim == 128 ? launch_attention_typed<uint16_t, 128>(p, plan.MB, stream)
-                            : launch_attention_typed<uint16_t, 64>(p, plan.MB, stream);
+    e = kv->head_dim == 128 ? launch_attention_typed<uint16_t, 128>(p, plan.groups, stream)
+                            : launch_attention_typed<uint16_t, 64>(p, plan.groups, stream);
   else
-    e = kv->head_dim == 128 ? launch_attention_typed<float, 128>(p, plan.MB, stream)
-                            : launch_attention_typed<float, 64>(p, plan.MB, stream);
+    e = kv->head_dim == 128 ? launch_attention_typed<float, 128>(p, plan.groups, stream)
+                            : launch_attention_typed<float, 64>(p, plan.groups, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 

@@ -181,6 +181,65 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(GemmParams p) {
   }
 }
 
+// U = x A^T for the LoRA (r <= 128 columns): split-K over kUSplit slices so
+// a 512 x 4096 problem still spreads over 128 workgroups. Each wave reduces
+// a quarter of its slice, the waves are summed in order through LDS, and the
+// slices are summed in order by lora_u_reduce_kernel: a fixed reduction
+// order for every element whatever M is.
+constexpr int kUSplit = 8;
+
+__global__ __launch_bounds__(256) void lora_u_partial_kernel(const uint16_t* x, const uint16_t* A, float* upart,
+                                                             int M, int K, int r) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lane32 = lane & 31, hh = lane >> 5;
+  const int m0 = blockIdx.x * 32, ks = blockIdx.y;
+  // k-steps of 16 split evenly over the kUSplit * 4 waves of the grid row
+  const int T = K / 16, gw = ks * 4 + wave;
+  const int s_begin = (gw * T) / (kUSplit * 4), s_end = ((gw + 1) * T) / (kUSplit * 4);
+  const int row = m0 + lane32;
+  const int nblk = (r + 31) / 32;
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  for (int st = s_begin; st < s_end; ++st) {
+    const int k = 16 * st;
+    const u32x4 av = row < M ? *reinterpret_cast<const u32x4*>(x + static_cast<long>(row) * K + k + 8 * hh)
+                             : u32x4{0, 0, 0, 0};
+    const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < nblk) {
+        const int col = 32 * j + lane32;
+        const u32x4 bv = col < r ? *reinterpret_cast<const u32x4*>(A + static_cast<long>(col) * K + k + 8 * hh)
+                                 : u32x4{0, 0, 0, 0};
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+      }
+    }
+  }
+  __shared__ float red[4][32][129];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < nblk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave][8 * (e >> 2) + 4 * hh + (e & 3)][32 * j + lane32] = acc[j][e];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
+    const int i = idx / r, c = idx % r;
+    if (m0 + i >= M) continue;
+    const float v = ((red[0][i][c] + red[1][i][c]) + red[2][i][c]) + red[3][i][c];
+    upart[(static_cast<long>(ks) * M + m0 + i) * r + c] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void lora_u_reduce_kernel(const float* upart, float* U, int M, int r) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(M) * r) return;
+  float v = upart[idx];
+#pragma unroll
+  for (int ks = 1; ks < kUSplit; ++ks) v += upart[static_cast<long>(ks) * M * r + idx];
+  U[idx] = v;
+}
+
 }  // namespace isd
 
 // ================================================================ host API
@@ -189,18 +248,34 @@ using namespace isd;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Tile choice depends only on the problem's (M, Nout), and the reduction
-// order inside a tile is the same for every choice.
+// Tile choice depends only on the problem's (M, Nout): the largest of
+// 128x128, 128x64 and 64x64 that still gives one workgroup per CU. The
+// reduction order inside a tile is the same for every choice.
 template <bool GATED>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
-  const long big = static_cast<long>((p.M + 127) / 128) * ((p.Nout + 127) / 128);
-  if (big >= 256) {
-    const dim3 grid((p.Nout + 127) / 128, (p.M + 127) / 128);
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, GATED>), grid, dim3(256), 0, stream, p);
+  auto wgs = [&](int bm, int bn) { return static_cast<long>((p.M + bm - 1) / bm) * ((p.Nout + bn - 1) / bn); };
+  if (wgs(128, 128) >= 256) {
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, GATED>), dim3((p.Nout + 127) / 128, (p.M + 127) / 128), dim3(256),
+                       0, stream, p);
+  } else if (wgs(128, 64) >= 256) {
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, GATED>), dim3((p.Nout + 63) / 64, (p.M + 127) / 128), dim3(256), 0,
+                       stream, p);
   } else {
-    const dim3 grid((p.Nout + 63) / 64, (p.M + 63) / 64);
-    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, GATED>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, GATED>), dim3((p.Nout + 63) / 64, (p.M + 63) / 64), dim3(256), 0,
+                       stream, p);
   }
+  return hipGetLastError();
+}
+
+// U = x A^T into ws (the first M*r floats), split-K partials after it.
+hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
+  float* U = static_cast<float*>(ws);
+  float* upart = U + static_cast<size_t>(M) * r;
+  hipLaunchKernelGGL(lora_u_partial_kernel, dim3((M + 31) / 32, kUSplit), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(A), upart, M, K, r);
+  const long n = static_cast<long>(M) * r;
+  hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, upart,
+                     U, M, r);
   return hipGetLastError();
 }
 
@@ -217,7 +292,7 @@ int check_lora_args(const void* A, const void* B, const uint8_t* mask, int r, vo
   if (!A || !B || !mask) return ISD_E_INVALID;
   if (r < 16 || r > 128 || r % 16 != 0) return ISD_E_UNSUPPORTED;
   if (!aligned16(A)) return ISD_E_INVALID;
-  const size_t need = static_cast<size_t>(M) * r * sizeof(float);
+  const size_t need = static_cast<size_t>(M) * r * sizeof(float) * (1 + kUSplit);
   if (!ws || ws_bytes < need || !aligned16(ws)) return ISD_E_WORKSPACE;
   return ISD_OK;
 }
@@ -243,7 +318,7 @@ int isd_linear(const void* x, const void* W, int M, int K, int Nout, float* y, h
 
 size_t isd_lora_workspace_size(int M, int r) {
   if (M < 0 || r < 0) return 0;
-  return static_cast<size_t>(M) * r * sizeof(float);
+  return static_cast<size_t>(M) * r * sizeof(float) * (1 + kUSplit);
 }
 
 int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t* is_mask, int M, int K, int Nout,
@@ -254,14 +329,7 @@ int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t*
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  GemmParams u{};
-  u.x = static_cast<const uint16_t*>(x);
-  u.w = static_cast<const uint16_t*>(A);
-  u.y = static_cast<float*>(ws);
-  u.M = M;
-  u.K = K;
-  u.Nout = r;
-  if (launch_gemm<false>(u, stream) != hipSuccess) return ISD_E_LAUNCH;
+  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.y = y;
   p.M = M;
@@ -285,14 +353,7 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  GemmParams u{};
-  u.x = static_cast<const uint16_t*>(x);
-  u.w = static_cast<const uint16_t*>(A);
-  u.y = static_cast<float*>(ws);
-  u.M = M;
-  u.K = K;
-  u.Nout = r;
-  if (launch_gemm<false>(u, stream) != hipSuccess) return ISD_E_LAUNCH;
+  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);

@@ -76,10 +76,10 @@ int isd_version(void);
  * Physical layout of one page, chosen so that every MFMA operand the
  * attention kernel needs is a run of 16 contiguous bytes:
  *   K: [num_kv_heads][head_dim / KP][16 slots][KP]    KP = 16 / sizeof(elem)
- *   V: [num_kv_heads][head_dim][16 slots]
+ *   V: [num_kv_heads][2 half-pages][head_dim][8 slots]
  * i.e. for bf16, element (slot s, head g, dim d) of page p is at
  *   k_pages[((p*Hkv + g)*(D/8) + d/8)*16*8 + s*8 + d%8]
- *   v_pages[((p*Hkv + g)*D + d)*16 + s].
+ *   v_pages[((p*Hkv + g)*2 + s/8)*D*8 + d*8 + s%8].
  * Position t of sequence b lives in page block_table[b*table_stride + t/16],
  * slot t%16. Entries of the block table past a sequence's length are never
  * read.
@@ -117,18 +117,22 @@ int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
  *   ctx  [C] cached tokens before the block
  *   Query head h reads KV head h / (Hq / Hkv). scale multiplies q.k
  *   (1/sqrt(D) in the usual model). max_len is a host-side upper bound of
- *   ctx[b] + rows over the batch; it sizes the grid. chunk (0 = automatic,
- *   else a multiple of 32) is the KV span one workgroup reduces before a
- *   log-sum-exp merge; the workspace size depends on it.
+ *   ctx[b] + rows, used only to size the launch (results do not depend on
+ *   it). The 32-key tiles of all sequences are split evenly over `slices`
+ *   workgroups per group of KV heads (0 = automatic: one per CU for 8B and
+ *   32B shapes); sequences shared by several workgroups are merged with a
+ *   log-sum-exp combine in a fixed order, so results do not depend on
+ *   scheduling. The workspace (size from isd_attention_workspace_size with
+ *   the same arguments) holds those partial results; no initialisation.
  * Supported: D in {64, 128}; Hq multiple of Hkv; (Hq/Hkv)*rows <= 128;
- * rows <= 64.
+ * rows <= 64; C <= 8192.
  */
 size_t isd_attention_workspace_size(int C, int rows, int num_q_heads,
                                     const isd_kv_cache* kv, int max_len,
-                                    int chunk);
+                                    int slices);
 int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx,
                   int C, int rows, int num_q_heads, float scale, int max_len,
-                  int chunk, float* out, void* ws, size_t ws_bytes,
+                  int slices, float* out, void* ws, size_t ws_bytes,
                   int32_t* dev_err, hipStream_t stream);
 
 /* ---------------------------------------------------------- accept
@@ -183,6 +187,7 @@ typedef struct isd_accept_args {
   int32_t* n_emit;    /* [C] */
   int32_t* emit;      /* [C][N], -1 past n_emit */
   int32_t* kv_commit; /* [C] */
+  int32_t* ctx;       /* optional [C]: ctx[b] += kv_commit[b] (the commit) */
   float* p_x;         /* optional [C][N-1]: P_{j-1}(x_j) of tested drafts */
   float* resid_mass;  /* optional [C]: sum max(0, P_a - Q_{a+1}), or -1 */
   float* row_m;       /* optional [C][rows]: max logit of each row read */

@@ -64,17 +64,20 @@ def test_attention_rejects_bad_arguments_on_host(lib):
     kv.num_kv_heads = 1
     # group * rows > 128
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 40, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
-    # scale must be positive, chunk a multiple of 32, max_len >= rows
+    # scale must be positive, slices >= 0, max_len >= rows
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, -1.0, 64, 0, 16, None, 0, None, None) == -1
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 48, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -3, 16, None, 0, None, None) == -1
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4, 0, 16, None, 0, None, None) == -1
     # misaligned q
     assert lib.isd_attention(ctypes.byref(kv), 18, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -1
-    # a split that needs a workspace and gets none
+    # too many sequences for one call
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 9000, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    # the workspace is required and sized by the same arguments
     need = lib.isd_attention_workspace_size(1, 8, 4, ctypes.byref(kv), 4096, 64)
     assert need > 0
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, None, 0, None, None) == -3
-    assert lib.isd_attention_workspace_size(1, 8, 4, ctypes.byref(kv), 64, 64) == 0
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, 1 << 20, need - 16, None,
+                             None) == -3
 
 
 def test_accept_rejects_bad_arguments_on_host(lib):
@@ -107,4 +110,4 @@ def test_linear_rejects_bad_arguments_on_host(lib):
     assert lib.isd_linear(16, 16, 0, 64, 8, 16, None) == 0  # empty problem
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, 16, 1 << 20, None) == -2  # rank 24
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 16, 8, None) == -3  # ws too small
-    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4
+    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4 * 9  # U plus 8 split-K partials

@@ -45,12 +45,12 @@ def slab_errors(got, want):
     return np.abs(g - w).max(-1) / np.abs(w).max(-1)
 
 
-def run(case, chunk=0, seqs=None):
+def run(case, slices=0, seqs=None):
     print(f"attention case C={case.C} rows={case.rows} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
-          f"{case.dtype} chunk={chunk}", flush=True)
+          f"{case.dtype} slices={slices}", flush=True)
     kv, err = fill_cache(case)
     out = dvd.isd_attention(kv, case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV),
-                            max_len=int(case.lengths.max()), chunk=chunk, dev_err=err)
+                            max_len=int(case.lengths.max()), slices=slices, dev_err=err)
     torch.cuda.synchronize()
     assert err.item() == 0
     got = out.cpu().double().numpy()
@@ -71,13 +71,13 @@ def test_kv_write_matches_documented_page_layout():
     kp, vp = oracle_pages(case)  # [P, 16, Hkv, D] plain layout
     P, Hkv, D = case.num_pages, case.Hkv, case.D
     k_dev = to64(kv.k_pages).reshape(P, Hkv, D // 8, 16, 8)
-    v_dev = to64(kv.v_pages).reshape(P, Hkv, D, 16)
+    v_dev = to64(kv.v_pages).reshape(P, Hkv, 2, D, 8)
     used = sorted(set(case.table[case.table >= 0].ravel().tolist()))
     for b in range(case.C):
         for t in range(int(case.lengths[b])):
             p, s = case.table[b, t // 16], t % 16
             assert np.array_equal(k_dev[p, :, :, s, :].reshape(Hkv, D), kp[p, s])
-            assert np.array_equal(v_dev[p, :, :, s], vp[p, s])
+            assert np.array_equal(v_dev[p, :, s // 8, :, s % 8], vp[p, s])
     unused = sorted(set(range(P)) - set(used))
     assert unused and not k_dev[unused].any()
 
@@ -89,11 +89,12 @@ def test_tiny_fp32_config():
     assert slab_errors(got, want).max() < 1e-5
 
 
-@pytest.mark.parametrize("chunk", [0, 64, 96])
-def test_bf16_gqa_ragged_contexts(chunk):
-    """8B-class heads (32/8, D=128), several tiles, ragged tails, split-KV."""
+@pytest.mark.parametrize("slices", [0, 1, 3, 7, 41])
+def test_bf16_gqa_ragged_contexts(slices):
+    """8B-class heads (32/8, D=128), several tiles, ragged tails; slices
+    from one workgroup for everything to several per sequence (merges)."""
     case = workload.AttentionCase(11, C=5, rows=8, Hq=32, Hkv=8, D=128, ctx=[0, 1, 31, 100, 1000])
-    got, want = run(case, chunk=chunk)
+    got, want = run(case, slices=slices)
     e = slab_errors(got, want)
     print("max slab error", e.max())
     assert e.max() < 2e-3
@@ -103,7 +104,7 @@ def test_bf16_gqa_ragged_contexts(chunk):
 def test_32b_class_heads_strides(N):
     """64/8 heads: the GQA pack is 8 * 2N query rows (16..128)."""
     case = workload.AttentionCase(20 + N, C=2, rows=2 * N, Hq=64, Hkv=8, D=128, ctx=[333, 1290])
-    got, want = run(case, chunk=256)
+    got, want = run(case, slices=5)
     assert slab_errors(got, want).max() < 2e-3
 
 
@@ -120,7 +121,7 @@ def test_head_dim_64_bf16_and_single_token_context():
 def test_largest_query_pack_and_rows():
     """rows = 64 with group 2 (128 query columns)."""
     case = workload.AttentionCase(41, C=2, rows=64, Hq=4, Hkv=2, D=128, ctx=[10, 300])
-    got, want = run(case, chunk=128)
+    got, want = run(case, slices=9)
     assert slab_errors(got, want).max() < 2e-3
 
 
@@ -137,8 +138,8 @@ def test_outputs_are_deterministic():
     case = workload.AttentionCase(5, C=4, rows=8, Hq=32, Hkv=8, D=128, ctx=[700, 2000, 64, 3000])
     kv, err = fill_cache(case)
     q, ctx = case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV)
-    a = dvd.isd_attention(kv, q, ctx, max_len=3008, chunk=256)
-    b = dvd.isd_attention(kv, q, ctx, max_len=3008, chunk=256)
+    a = dvd.isd_attention(kv, q, ctx, max_len=3008, slices=13)
+    b = dvd.isd_attention(kv, q, ctx, max_len=3008, slices=13)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
