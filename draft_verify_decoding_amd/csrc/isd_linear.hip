@@ -8,12 +8,15 @@
 //
 // GEMM: y[M][Nout] fp32 = x[M][K] bf16 . W[Nout][K]^T bf16 ("NT": both
 // operands K-contiguous). Workgroup tile 2*WM x 2*WN (four waves, each WM x WN
-// in 32x32 MFMA blocks), K in steps of 64 through double-buffered LDS with
-// padded rows (72 elements) so the 16-byte operand reads are conflict-free.
-// The per-output reduction order is K-step by K-step in ascending K and does
-// not depend on M, the tile choice, the other rows or the mask.
-// LoRA: U = x A^T (same GEMM, fp32 out), then delta = U B^T on MFMA
-// 32x32x2 f32 (B widened exactly), added with one fma only to MASK rows.
+// in 32x32 MFMA blocks), K in slabs of 64 through double-buffered LDS with
+// padded rows (72 elements) so the 16-byte operand reads are conflict-free,
+// several slabs in flight in a register ring. The per-output reduction order
+// is slab by slab in ascending K and does not depend on M, the tile choice,
+// the other rows or the mask.
+// LoRA: U = x A^T comes out of the same GEMM as r extra output columns (A's
+// rows appended to W's); delta = U B^T then runs on bf16 MFMA with U split
+// into bf16 high and low halves (about 16 mantissa bits), and is added with
+// one fma to MASK rows only.
 #include "isd_common.hpp"
 
 namespace isd {
@@ -21,37 +24,16 @@ namespace isd {
 constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // elements per LDS row
 
-// delta tile (rows m0.., cols n0..) = U[m0:m0+32][0:r] . B[n0:n0+32][0:r]^T in
-// the 32x32 MFMA accumulator layout: register e of lane (j, hh) is row
-// m0 + 8(e/4) + 4hh + e%4, column n0 + j.
-__device__ __forceinline__ f32x16 lora_delta_tile(const float* U, int r, const uint16_t* B, int m0, int n0, int M,
-                                                  int Nout, int lane) {
-  const int i = lane & 31, hh = lane >> 5;
-  const int row = m0 + i, col = n0 + i;
-  f32x16 acc = {};
-  for (int s = 0; s < r / 2; ++s) {
-    const int k = 2 * s + hh;
-    const float a = row < M ? U[static_cast<long>(row) * r + k] : 0.f;
-    const float bb = col < Nout ? bf16_bits_to_f32(B[static_cast<long>(col) * r + k]) : 0.f;
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
-  }
-  return acc;
-}
-
 struct GemmParams {
   const uint16_t* x;  // [M][K]
   const uint16_t* w;  // [Nout][K]
+  const uint16_t* a;  // optional [r][K]: output columns Nout..Nout+r-1 use A's rows
   float* y;           // [M][Nout]
-  int M, K, Nout;
-  // gated epilogue
-  const float* U;        // [M][r]
-  const uint16_t* B;     // [Nout][r]
-  const uint8_t* mask;   // [M]
-  int r;
-  float scale;
+  float* u;           // [M][r] receives x A^T when a != nullptr
+  int M, K, Nout, r;
 };
 
-template <int WM, int WN, bool GATED>
+template <int WM, int WN, int DEPTH>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   constexpr int BM = 2 * WM, BN = 2 * WN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -68,30 +50,32 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   const int m_blk = blockIdx.y * BM, n_blk = blockIdx.x * BN;
 
   // Global->register staging: thread loads rows (tid / 8) + 32*q, 16 bytes at
-  // column 8 * (tid % 8) of the 64-wide K slab.
+  // column 8 * (tid % 8) of the 64-wide K slab. A ring of DEPTH register
+  // sets keeps DEPTH slabs in flight; LDS is double-buffered.
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
-  u32x4 ra[A_ROUNDS], rb[B_ROUNDS];
-  auto load_slab = [&](int k0) {
+  u32x4 ra[DEPTH][A_ROUNDS], rb[DEPTH][B_ROUNDS];
+  auto load_slab = [&](int k0, u32x4 (&a)[A_ROUNDS], u32x4 (&b)[B_ROUNDS]) {
 #pragma unroll
     for (int q = 0; q < A_ROUNDS; ++q) {
       const int row = m_blk + ld_row + 32 * q;
-      ra[q] = row < p.M ? *reinterpret_cast<const u32x4*>(p.x + static_cast<long>(row) * p.K + k0 + ld_col)
-                        : u32x4{0, 0, 0, 0};
+      a[q] = row < p.M ? *reinterpret_cast<const u32x4*>(p.x + static_cast<long>(row) * p.K + k0 + ld_col)
+                       : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int q = 0; q < B_ROUNDS; ++q) {
       const int row = n_blk + ld_row + 32 * q;
-      rb[q] = row < p.Nout ? *reinterpret_cast<const u32x4*>(p.w + static_cast<long>(row) * p.K + k0 + ld_col)
-                           : u32x4{0, 0, 0, 0};
+      const uint16_t* src = row < p.Nout ? p.w + static_cast<long>(row) * p.K
+                                         : (row < p.Nout + p.r ? p.a + static_cast<long>(row - p.Nout) * p.K : nullptr);
+      b[q] = src ? *reinterpret_cast<const u32x4*>(src + k0 + ld_col) : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_slab = [&](int buf) {
+  auto store_slab = [&](int buf, const u32x4 (&a)[A_ROUNDS], const u32x4 (&b)[B_ROUNDS]) {
 #pragma unroll
     for (int q = 0; q < A_ROUNDS; ++q)
-      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = ra[q];
+      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = a[q];
 #pragma unroll
     for (int q = 0; q < B_ROUNDS; ++q)
-      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = rb[q];
+      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = b[q];
   };
 
   f32x16 acc[TM][TN];
@@ -100,13 +84,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  const int nk = p.K / kBK;
-  load_slab(0);
-  store_slab(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_slab((kt + 1) * kBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       bf16x8 a[TM], b[TN];
@@ -123,121 +101,127 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      store_slab(buf ^ 1);
-      __syncthreads();
+  };
+
+  const int nk = p.K / kBK;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nk) load_slab(d * kBK, ra[d], rb[d]);
+  store_slab(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < nk; kt0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int kt = kt0 + d;
+      if (kt < nk) {
+        compute(kt & 1);
+        // slab kt+1 (in ring slot d+1) goes to the other LDS buffer; ring
+        // slot d, whose slab is already in LDS, is refilled with kt+DEPTH
+        if (kt + 1 < nk) store_slab((kt + 1) & 1, ra[(d + 1) % DEPTH], rb[(d + 1) % DEPTH]);
+        if (kt + DEPTH < nk) load_slab((kt + DEPTH) * kBK, ra[d], rb[d]);
+        __syncthreads();
+      }
     }
   }
 
   // Epilogue: register e of lane (j, hh) is row 8(e/4) + 4hh + e%4 of the
-  // 32x32 block, column j.
+  // 32x32 block, column j; columns past Nout are the U = x A^T columns.
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int m0 = m_blk + wm + 32 * i, n0 = n_blk + wn + 32 * j;
-      if constexpr (GATED) {
-        bool any = false;
-        const int rrow = m0 + lane32;
-        if (rrow < p.M) any = p.mask[rrow] != 0;
-        if (__any(any)) {
-          const f32x16 dl = lora_delta_tile(p.U, p.r, p.B, m0, n0, p.M, p.Nout, lane);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (row < p.M && p.mask[row]) acc[i][j][e] = fmaf(p.scale, dl[e], acc[i][j][e]);
-          }
-        }
-      }
       const int col = n0 + lane32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (row < p.M && col < p.Nout) p.y[static_cast<long>(row) * p.Nout + col] = acc[i][j][e];
+        if (row >= p.M) continue;
+        if (col < p.Nout)
+          p.y[static_cast<long>(row) * p.Nout + col] = acc[i][j][e];
+        else if (col < p.Nout + p.r)
+          p.u[static_cast<long>(row) * p.r + (col - p.Nout)] = acc[i][j][e];
       }
     }
 }
 
-// y[m] += scale * delta on MASK rows only, one wave per 32x32 tile.
-__global__ __launch_bounds__(256) void lora_delta_kernel(GemmParams p) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, hh = lane >> 5;
+// y[m] += scale * (U B^T)[m] on MASK rows only, one wave per 32x32 tile of
+// y; tiles without a MASK row are skipped. U (fp32) is split into bf16 high
+// and low halves, so the product runs on bf16 MFMA (32x32x16) with both
+// operands read as 16-byte runs. Every load of a wave (its mask bytes, all of
+// U and B for the tile, then y of its MASK rows) is issued before the first
+// MFMA, so a tile costs about two memory round trips. Clean rows are never
+// written.
+struct DeltaParams {
+  const float* u;      // [M][r]
+  const uint16_t* b;   // [Nout][r]
+  const uint8_t* mask; // [M]
+  float* y;            // [M][Nout]
+  int M, Nout, r;
+  float scale;
+};
+
+template <int R16>  // r / 16
+__global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lane32 = lane & 31, hh = lane >> 5;
   const int tiles_n = (p.Nout + 31) / 32;
   const long tile = static_cast<long>(blockIdx.x) * 4 + wave;
   if (tile >= static_cast<long>((p.M + 31) / 32) * tiles_n) return;
   const int m0 = static_cast<int>(tile / tiles_n) * 32, n0 = static_cast<int>(tile % tiles_n) * 32;
-  const int rrow = m0 + (lane & 31);
-  const bool mine = rrow < p.M && p.mask[rrow] != 0;
+  const int arow = m0 + lane32, bcol = n0 + lane32;
+  const int mine = arow < p.M ? p.mask[arow] != 0 : 0;
   if (!__any(mine)) return;
-  const f32x16 dl = lora_delta_tile(p.U, p.r, p.B, m0, n0, p.M, p.Nout, lane);
-  const int col = n0 + (lane & 31);
-  if (col >= p.Nout) return;
+
+  f32x4 uv[R16][2];
+  u32x4 bv[R16];
+#pragma unroll
+  for (int k = 0; k < R16; ++k) {
+    if (arow < p.M) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.u + static_cast<long>(arow) * p.r + 16 * k + 8 * hh);
+      uv[k][0] = src[0];
+      uv[k][1] = src[1];
+    } else {
+      uv[k][0] = uv[k][1] = f32x4{};
+    }
+    bv[k] = bcol < p.Nout ? *reinterpret_cast<const u32x4*>(p.b + static_cast<long>(bcol) * p.r + 16 * k + 8 * hh)
+                          : u32x4{0, 0, 0, 0};
+  }
+  // register e holds row 8(e/4) + 4hh + e%4 of the tile; its mask bit sits
+  // in the lane whose U row that is
+  float yv[16];
+  int live = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-    if (row < p.M && p.mask[row]) {
-      float* yp = p.y + static_cast<long>(row) * p.Nout + col;
-      *yp = fmaf(p.scale, dl[e], *yp);
+    const int rl = 8 * (e >> 2) + 4 * hh + (e & 3);
+    const int on = __shfl(mine, rl) && bcol < p.Nout;
+    live |= on << e;
+    yv[e] = on ? p.y[static_cast<long>(m0 + rl) * p.Nout + bcol] : 0.f;
+  }
+
+  f32x16 dl = {};
+#pragma unroll
+  for (int k = 0; k < R16; ++k) {
+    const float f[8] = {uv[k][0][0], uv[k][0][1], uv[k][0][2], uv[k][0][3],
+                        uv[k][1][0], uv[k][1][1], uv[k][1][2], uv[k][1][3]};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t ua = __float_as_uint(f[2 * t]) & 0xffff0000u, ub = __float_as_uint(f[2 * t + 1]) & 0xffff0000u;
+      hi[t] = (ua >> 16) | ub;
+      lo[t] = f32_to_bf16_bits(f[2 * t] - __uint_as_float(ua)) |
+              (f32_to_bf16_bits(f[2 * t + 1] - __uint_as_float(ub)) << 16);
+    }
+    const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[k]);
+    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi), bb, dl, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo), bb, dl, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if ((live >> e) & 1) {
+      const int rl = 8 * (e >> 2) + 4 * hh + (e & 3);
+      p.y[static_cast<long>(m0 + rl) * p.Nout + bcol] = fmaf(p.scale, dl[e], yv[e]);
     }
   }
-}
-
-// U = x A^T for the LoRA (r <= 128 columns): split-K over kUSplit slices so
-// a 512 x 4096 problem still spreads over 128 workgroups. Each wave reduces
-// a quarter of its slice, the waves are summed in order through LDS, and the
-// slices are summed in order by lora_u_reduce_kernel: a fixed reduction
-// order for every element whatever M is.
-constexpr int kUSplit = 8;
-
-__global__ __launch_bounds__(256) void lora_u_partial_kernel(const uint16_t* x, const uint16_t* A, float* upart,
-                                                             int M, int K, int r) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int lane32 = lane & 31, hh = lane >> 5;
-  const int m0 = blockIdx.x * 32, ks = blockIdx.y;
-  // k-steps of 16 split evenly over the kUSplit * 4 waves of the grid row
-  const int T = K / 16, gw = ks * 4 + wave;
-  const int s_begin = (gw * T) / (kUSplit * 4), s_end = ((gw + 1) * T) / (kUSplit * 4);
-  const int row = m0 + lane32;
-  const int nblk = (r + 31) / 32;
-  f32x16 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
-  for (int st = s_begin; st < s_end; ++st) {
-    const int k = 16 * st;
-    const u32x4 av = row < M ? *reinterpret_cast<const u32x4*>(x + static_cast<long>(row) * K + k + 8 * hh)
-                             : u32x4{0, 0, 0, 0};
-    const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < nblk) {
-        const int col = 32 * j + lane32;
-        const u32x4 bv = col < r ? *reinterpret_cast<const u32x4*>(A + static_cast<long>(col) * K + k + 8 * hh)
-                                 : u32x4{0, 0, 0, 0};
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
-      }
-    }
-  }
-  __shared__ float red[4][32][129];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (j < nblk)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave][8 * (e >> 2) + 4 * hh + (e & 3)][32 * j + lane32] = acc[j][e];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
-    const int i = idx / r, c = idx % r;
-    if (m0 + i >= M) continue;
-    const float v = ((red[0][i][c] + red[1][i][c]) + red[2][i][c]) + red[3][i][c];
-    upart[(static_cast<long>(ks) * M + m0 + i) * r + c] = v;
-  }
-}
-
-__global__ __launch_bounds__(256) void lora_u_reduce_kernel(const float* upart, float* U, int M, int r) {
-  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long>(M) * r) return;
-  float v = upart[idx];
-#pragma unroll
-  for (int ks = 1; ks < kUSplit; ++ks) v += upart[static_cast<long>(ks) * M * r + idx];
-  U[idx] = v;
 }
 
 }  // namespace isd
@@ -248,34 +232,48 @@ using namespace isd;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Tile choice depends only on the problem's (M, Nout): the largest of
-// 128x128, 128x64 and 64x64 that still gives one workgroup per CU. The
+// Tile choice depends only on the problem's (M, output columns): 128x128
+// when that still gives one workgroup per CU, else 64x64 (measured faster
+// than 128x64 at the projection shapes of a 64-sequence stride batch). The
 // reduction order inside a tile is the same for every choice.
-template <bool GATED>
+constexpr int kDepth = 3;  // K slabs in flight per thread
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
-  auto wgs = [&](int bm, int bn) { return static_cast<long>((p.M + bm - 1) / bm) * ((p.Nout + bn - 1) / bn); };
-  if (wgs(128, 128) >= 256) {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, GATED>), dim3((p.Nout + 127) / 128, (p.M + 127) / 128), dim3(256),
-                       0, stream, p);
-  } else if (wgs(128, 64) >= 256) {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, GATED>), dim3((p.Nout + 63) / 64, (p.M + 127) / 128), dim3(256), 0,
+  const int cols = p.Nout + (p.a ? p.r : 0);
+  const long big = static_cast<long>((p.M + 127) / 128) * ((cols + 127) / 128);
+  if (big >= 256) {
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth>), dim3((cols + 127) / 128, (p.M + 127) / 128), dim3(256), 0,
                        stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, GATED>), dim3((p.Nout + 63) / 64, (p.M + 63) / 64), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth>), dim3((cols + 63) / 64, (p.M + 63) / 64), dim3(256), 0,
                        stream, p);
   }
   return hipGetLastError();
 }
 
-// U = x A^T into ws (the first M*r floats), split-K partials after it.
-hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
-  float* U = static_cast<float*>(ws);
-  float* upart = U + static_cast<size_t>(M) * r;
-  hipLaunchKernelGGL(lora_u_partial_kernel, dim3((M + 31) / 32, kUSplit), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(A), upart, M, K, r);
-  const long n = static_cast<long>(M) * r;
-  hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, upart,
-                     U, M, r);
+hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int M, int Nout, int r, float scale,
+                        float* y, hipStream_t stream) {
+  DeltaParams d{};
+  d.u = U;
+  d.b = static_cast<const uint16_t*>(B);
+  d.mask = mask;
+  d.y = y;
+  d.M = M;
+  d.Nout = Nout;
+  d.r = r;
+  d.scale = scale;
+  const long tiles = static_cast<long>((M + 31) / 32) * ((Nout + 31) / 32);
+  const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
+  switch (r / 16) {
+    case 1: hipLaunchKernelGGL(lora_delta_kernel<1>, grid, dim3(256), 0, stream, d); break;
+    case 2: hipLaunchKernelGGL(lora_delta_kernel<2>, grid, dim3(256), 0, stream, d); break;
+    case 3: hipLaunchKernelGGL(lora_delta_kernel<3>, grid, dim3(256), 0, stream, d); break;
+    case 4: hipLaunchKernelGGL(lora_delta_kernel<4>, grid, dim3(256), 0, stream, d); break;
+    case 5: hipLaunchKernelGGL(lora_delta_kernel<5>, grid, dim3(256), 0, stream, d); break;
+    case 6: hipLaunchKernelGGL(lora_delta_kernel<6>, grid, dim3(256), 0, stream, d); break;
+    case 7: hipLaunchKernelGGL(lora_delta_kernel<7>, grid, dim3(256), 0, stream, d); break;
+    default: hipLaunchKernelGGL(lora_delta_kernel<8>, grid, dim3(256), 0, stream, d); break;
+  }
   return hipGetLastError();
 }
 
@@ -291,8 +289,8 @@ int check_gemm_args(const void* x, const void* W, int M, int K, int Nout, const 
 int check_lora_args(const void* A, const void* B, const uint8_t* mask, int r, void* ws, size_t ws_bytes, int M) {
   if (!A || !B || !mask) return ISD_E_INVALID;
   if (r < 16 || r > 128 || r % 16 != 0) return ISD_E_UNSUPPORTED;
-  if (!aligned16(A)) return ISD_E_INVALID;
-  const size_t need = static_cast<size_t>(M) * r * sizeof(float) * (1 + kUSplit);
+  if (!aligned16(A) || !aligned16(B)) return ISD_E_INVALID;
+  const size_t need = static_cast<size_t>(M) * r * sizeof(float);
   if (!ws || ws_bytes < need || !aligned16(ws)) return ISD_E_WORKSPACE;
   return ISD_OK;
 }
@@ -313,12 +311,12 @@ int isd_linear(const void* x, const void* W, int M, int K, int Nout, float* y, h
   p.M = M;
   p.K = K;
   p.Nout = Nout;
-  return launch_gemm<false>(p, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+  return launch_gemm(p, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
 size_t isd_lora_workspace_size(int M, int r) {
   if (M < 0 || r < 0) return 0;
-  return static_cast<size_t>(M) * r * sizeof(float) * (1 + kUSplit);
+  return static_cast<size_t>(M) * r * sizeof(float);
 }
 
 int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t* is_mask, int M, int K, int Nout,
@@ -329,20 +327,19 @@ int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t*
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
+  // U = x A^T through the projection GEMM (A's rows as the output columns),
+  // so U is bit-identical to the U columns of the fused call below.
   GemmParams p{};
-  p.y = y;
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = static_cast<const uint16_t*>(A);
+  p.y = static_cast<float*>(ws);
   p.M = M;
   p.K = K;
-  p.Nout = Nout;
-  p.U = static_cast<const float*>(ws);
-  p.B = static_cast<const uint16_t*>(B);
-  p.mask = is_mask;
-  p.r = r;
-  p.scale = scale;
-  const long tiles = static_cast<long>((M + 31) / 32) * ((Nout + 31) / 32);
-  hipLaunchKernelGGL(lora_delta_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4)), dim3(256), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+  p.Nout = r;
+  if (launch_gemm(p, stream) != hipSuccess) return ISD_E_LAUNCH;
+  return launch_delta(static_cast<const float*>(ws), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess
+             ? ISD_OK
+             : ISD_E_LAUNCH;
 }
 
 int isd_linear_gated(const void* x, const void* W, const void* A, const void* B, const uint8_t* is_mask, int M, int K,
@@ -353,20 +350,20 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
+  p.a = static_cast<const uint16_t*>(A);
   p.y = y;
+  p.u = static_cast<float*>(ws);
   p.M = M;
   p.K = K;
   p.Nout = Nout;
-  p.U = static_cast<const float*>(ws);
-  p.B = static_cast<const uint16_t*>(B);
-  p.mask = is_mask;
   p.r = r;
-  p.scale = scale;
-  return launch_gemm<true>(p, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+  if (launch_gemm(p, stream) != hipSuccess) return ISD_E_LAUNCH;
+  return launch_delta(static_cast<const float*>(ws), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess
+             ? ISD_OK
+             : ISD_E_LAUNCH;
 }
 
 }  // extern "C"

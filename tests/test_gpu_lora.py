@@ -45,9 +45,10 @@ def test_base_projection_8b_shapes(Nout):
     assert e < 1e-4
 
 
-@pytest.mark.parametrize("r", [32, 128])
-def test_gated_lora_8b_shapes(r):
-    x, W, A, B, mask = case(2, 512, 4096, 4096, r)
+@pytest.mark.parametrize("Nout,r", [(4096, 32), (4096, 128), (6144, 96)])
+def test_gated_lora_8b_shapes(Nout, r):
+    """O projection (4096) and fused Q|K|V (6144 = 4096 + 2 * 1024, r = 3 * 32)."""
+    x, W, A, B, mask = case(2, 512, 4096, Nout, r)
     xd, Wd, Ad, Bd = dev(x, W, A, B)
     md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
     base = dvd.isd_linear(xd, Wd)
@@ -113,3 +114,23 @@ def test_scaled_adapter_ragged():
     want = ref.gated_lora(x.double().numpy(), W.double().numpy(), A.double().numpy(),
                           B.double().numpy(), mask, 0.5)
     assert rel_err(y.cpu().double().numpy(), want) < 2e-3
+
+
+def test_large_batch_uses_the_wide_tile_with_same_bits():
+    """2048 rows (C=256, N=4) pick the 128x128 tile; sampled rows match the
+    oracle, and equal bit for bit the same rows computed in a small launch
+    (64x64 tile). The fused U columns straddle the last W tile."""
+    x, W, A, B, mask = case(6, 2048, 4096, 4096, 32)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    base = dvd.isd_linear(xd, Wd)
+    fused = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=2.0)
+    small = dvd.isd_linear_gated(xd[1000:1040].contiguous(), Wd, Ad, Bd, md[1000:1040].contiguous(), scale=2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(fused[1000:1040], small)
+    m = torch.from_numpy(mask).to(DEV)
+    assert torch.equal(fused[~m].view(torch.int32), base[~m].view(torch.int32))
+    rows = np.array([0, 1, 7, 513, 1000, 1031, 2046, 2047])
+    want = ref.gated_lora(x[rows].double().numpy(), W.double().numpy(), A.double().numpy(),
+                          B.double().numpy(), mask[rows], 2.0)
+    assert rel_err(fused.cpu()[rows].double().numpy(), want) < 2e-3
