@@ -11,6 +11,7 @@
 
 // 0 if the current HIP device is a gfx950, else ISD_E_DEVICE (isd_runtime.hip).
 extern "C" int isd_check_device_internal(void);
+extern "C" int isd_device_cus_internal(void);
 
 namespace isd {
 

@@ -51,23 +51,29 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 
   // Global->register staging: thread loads rows (tid / 8) + 32*q, 16 bytes at
   // column 8 * (tid % 8) of the 64-wide K slab. A ring of DEPTH register
-  // sets keeps DEPTH slabs in flight; LDS is double-buffered.
+  // sets keeps DEPTH slabs in flight; LDS is double-buffered. Every load is
+  // unconditional (no divergent branch around it), so the compiler waits
+  // only for the slab it is about to store: rows past the end read the last
+  // valid row instead. Output row i depends only on A row i and column j only
+  // on B row j, and such rows and columns are never written.
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
+  const uint16_t* a_src[A_ROUNDS];
+  const uint16_t* b_src[B_ROUNDS];
+#pragma unroll
+  for (int q = 0; q < A_ROUNDS; ++q)
+    a_src[q] = p.x + static_cast<long>(min(m_blk + ld_row + 32 * q, p.M - 1)) * p.K + ld_col;
+#pragma unroll
+  for (int q = 0; q < B_ROUNDS; ++q) {
+    const int row = min(n_blk + ld_row + 32 * q, p.Nout + p.r - 1);
+    b_src[q] = (row < p.Nout ? p.w + static_cast<long>(row) * p.K : p.a + static_cast<long>(row - p.Nout) * p.K) +
+               ld_col;
+  }
   u32x4 ra[DEPTH][A_ROUNDS], rb[DEPTH][B_ROUNDS];
   auto load_slab = [&](int k0, u32x4 (&a)[A_ROUNDS], u32x4 (&b)[B_ROUNDS]) {
 #pragma unroll
-    for (int q = 0; q < A_ROUNDS; ++q) {
-      const int row = m_blk + ld_row + 32 * q;
-      a[q] = row < p.M ? *reinterpret_cast<const u32x4*>(p.x + static_cast<long>(row) * p.K + k0 + ld_col)
-                       : u32x4{0, 0, 0, 0};
-    }
+    for (int q = 0; q < A_ROUNDS; ++q) a[q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
 #pragma unroll
-    for (int q = 0; q < B_ROUNDS; ++q) {
-      const int row = n_blk + ld_row + 32 * q;
-      const uint16_t* src = row < p.Nout ? p.w + static_cast<long>(row) * p.K
-                                         : (row < p.Nout + p.r ? p.a + static_cast<long>(row - p.Nout) * p.K : nullptr);
-      b[q] = src ? *reinterpret_cast<const u32x4*>(src + k0 + ld_col) : u32x4{0, 0, 0, 0};
-    }
+    for (int q = 0; q < B_ROUNDS; ++q) b[q] = *reinterpret_cast<const u32x4*>(b_src[q] + k0);
   };
   auto store_slab = [&](int buf, const u32x4 (&a)[A_ROUNDS], const u32x4 (&b)[B_ROUNDS]) {
 #pragma unroll
@@ -103,24 +109,25 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     }
   };
 
+  // Slabs past the last are clamped to it: their loads and the final LDS
+  // store are harmless repeats whose data is never read.
   const int nk = p.K / kBK;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nk) load_slab(d * kBK, ra[d], rb[d]);
+  for (int d = 0; d < DEPTH; ++d) load_slab(min(d, nk - 1) * kBK, ra[d], rb[d]);
   store_slab(0, ra[0], rb[0]);
   __syncthreads();
   for (int kt0 = 0; kt0 < nk; kt0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int kt = kt0 + d;
-      if (kt < nk) {
-        compute(kt & 1);
-        // slab kt+1 (in ring slot d+1) goes to the other LDS buffer; ring
-        // slot d, whose slab is already in LDS, is refilled with kt+DEPTH
-        if (kt + 1 < nk) store_slab((kt + 1) & 1, ra[(d + 1) % DEPTH], rb[(d + 1) % DEPTH]);
-        if (kt + DEPTH < nk) load_slab((kt + DEPTH) * kBK, ra[d], rb[d]);
-        __syncthreads();
-      }
+      if (kt >= nk) break;
+      compute(kt & 1);
+      // slab kt+1 (in ring slot d+1) goes to the other LDS buffer, whose
+      // readers passed the previous barrier; ring slot d, whose slab is
+      // already in LDS, is refilled with slab kt+DEPTH
+      store_slab((kt + 1) & 1, ra[(d + 1) % DEPTH], rb[(d + 1) % DEPTH]);
+      load_slab(min(kt + DEPTH, nk - 1) * kBK, ra[d], rb[d]);
+      __syncthreads();
     }
   }
 
@@ -232,20 +239,27 @@ using namespace isd;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Tile choice depends only on the problem's (M, output columns): 128x128
-// when that still gives one workgroup per CU, else 64x64 (measured faster
-// than 128x64 at the projection shapes of a 64-sequence stride batch). The
-// reduction order inside a tile is the same for every choice.
+// Tile choice depends only on (M, output columns) and the CU count, never on
+// the data, and every choice gives each output the same reduction order.
+// 128x128 when that still gives one workgroup per CU. Otherwise 64x64 when
+// its workgroups spread evenly over the CUs (or fit in one round), else
+// 128x64: a CU that holds one 64x64 workgroup more than the others sets the
+// pace, because four resident 64x64 workgroups saturate its LDS bandwidth.
 constexpr int kDepth = 3;  // K slabs in flight per thread
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   const int cols = p.Nout + (p.a ? p.r : 0);
+  const long cus = isd_device_cus_internal();
   const long big = static_cast<long>((p.M + 127) / 128) * ((cols + 127) / 128);
-  if (big >= 256) {
+  const long small = static_cast<long>((p.M + 63) / 64) * ((cols + 63) / 64);
+  if (big >= cus) {
     hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth>), dim3((cols + 127) / 128, (p.M + 127) / 128), dim3(256), 0,
                        stream, p);
-  } else {
+  } else if (small <= cus || small % cus == 0) {
     hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth>), dim3((cols + 63) / 64, (p.M + 63) / 64), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth>), dim3((cols + 63) / 64, (p.M + 127) / 128), dim3(256), 0,
                        stream, p);
   }
   return hipGetLastError();
