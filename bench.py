@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ISD accepted tokens/s at C=64,N=4 (8B shapes); attn+accept HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
 CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, lora_rank=32,
            ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3)
@@ -62,6 +63,62 @@ def accept_bytes(n_draft, accepted, cfg):
     rows = int(np.sum(n_draft + N))
     resid = int(np.sum(accepted < n_draft)) * 2
     return (rows + resid) * V * 2
+
+
+def projection_flops(cfg):
+    """Algorithmic flops of the two gated projections of one layer: the base
+    product over all 2N*C rows plus the rank-r delta (x A^T then U B^T) on the
+    N*C MASK rows."""
+    C, N, H, r = cfg["C"], cfg["N"], cfg["hidden"], cfg["lora_rank"]
+    M, Mm = C * 2 * N, C * N
+    n_qkv = (cfg["Hq"] + 2 * cfg["Hkv"]) * cfg["D"]
+    qkv = 2 * M * H * n_qkv + 3 * 2 * Mm * r * (H + n_qkv // 3)
+    o = 2 * M * H * H + 2 * Mm * r * (H + H)
+    return qkv, o
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_hbm_traffic_c64_n4.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_verify_decoding_amd", "csrc", f)
+                  for f in ("isd_attention.hip", "isd_common.hpp")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per isd_attention call from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, or None when the attention source has changed
+    since they were taken (or they are missing)."""
+    try:
+        lines = [l for l in open(TRAFFIC_FILE) if l.startswith("RESULT ")]
+        rec = json.loads(lines[-1][len("RESULT "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
+def summarize_counters(root):
+    """Per-kernel mean of every counter in a rocprofv3 --pmc CSV output tree
+    (KiB per dispatch for FETCH_SIZE / WRITE_SIZE), one line per kernel and
+    counter."""
+    import collections
+    import csv
+    acc = collections.defaultdict(list)
+    for dirpath, _, files in os.walk(root):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, f)) as fh:
+                    for row in csv.DictReader(fh):
+                        acc[(row["Kernel_Name"], row["Counter_Name"])].append(float(row["Counter_Value"]))
+    for (k, c), v in sorted(acc.items()):
+        print(f"{c:28s} dispatches={len(v):5d} mean={sum(v) / len(v):.6g}  {k[:90]}")
 
 
 def build(cfg, steps_total, dev):
@@ -244,7 +301,12 @@ def main():
     ap.add_argument("--slices", type=int, default=0, help="attention workgroups per KV-head group (0 = automatic)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-kernel means of a rocprofv3 --pmc CSV output directory and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.copy_probe:
         torch.cuda.set_device(0)
         n = 1 << 29  # 2-byte elements: 1 GiB read + 1 GiB written per copy
@@ -301,15 +363,22 @@ def main():
     acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
     acc_out = dvd.AcceptOutputs(C, N, R, dev, diag=False)
 
+    # every call runs on torch's current stream, so torch's events bracket
+    # exactly the launches of that call
     ev = lambda: torch.cuda.Event(enable_timing=True)
     att_ev = [[(ev(), ev()) for _ in range(L)] for _ in range(K)]
+    proj_ev = [[(ev(), ev(), ev()) for _ in range(L)] for _ in range(K)]
     acc_ev = [(ev(), ev()) for _ in range(K)]
 
     def step(t, timed_idx=None):
         for l in range(L):
             c = layer_calls[l]
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][0].record()
             for f in c["qkv"]:
                 f()
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][1].record()
             c["kvw"]()
             if timed_idx is not None:
                 att_ev[timed_idx][l][0].record()
@@ -317,6 +386,8 @@ def main():
             if timed_idx is not None:
                 att_ev[timed_idx][l][1].record()
             c["o"]()
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][2].record()
         s_in, s_out = (s_a, s_b) if t % 2 == 0 else (s_b, s_a)
         if timed_idx is not None:
             acc_ev[timed_idx][0].record()
@@ -344,6 +415,9 @@ def main():
     tokens = int(np.sum(ctx_end - ctx_start))  # n_emit == kv_commit per sequence-step
 
     att_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in att_ev])  # [K, L]
+    qkv_ms = np.array([[a.elapsed_time(b) for a, b, _ in row] for row in proj_ev])
+    o_ms = np.array([[a_end.elapsed_time(c) for (_, _, c), (_, a_end) in zip(row, arow)]
+                     for row, arow in zip(proj_ev, att_ev)])  # attention end -> O projection end
     acc_ms = np.array([a.elapsed_time(b) for a, b in acc_ev])
     att_bytes = np.array([attention_bytes(ctxs[W + i], cfg) for i in range(K)])  # per launch, per step
     acc_bytes = np.array([accept_bytes(nds[W + i], accs[W + i], cfg) for i in range(K)])
@@ -392,6 +466,19 @@ def main():
         "tokens_per_forward": round(tokens / (K * C), 4),
         "mean_accepted": round(float(accs[W:].mean()), 4),
     }
+    qkv_flops, o_flops = projection_flops(cfg)
+    res["projection_us_per_launch"] = {"qkv_gated": round(float(qkv_ms.mean()) * 1e3, 2),
+                                       "o_gated": round(float(o_ms.mean()) * 1e3, 2)}
+    proj_tflops = (qkv_flops + o_flops) * K * L / ((np.sum(qkv_ms) + np.sum(o_ms)) / 1e3) / 1e12
+    res["projection_mfma"] = {"achieved": round(float(proj_tflops), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(float(proj_tflops) / MFMA_BF16_PEAK_TFLOPS, 4)}
+    rec = committed_traffic()
+    if rec is not None:
+        # counter bytes per call of the profiled run, and their ratio to that
+        # run's algorithmic bytes (contexts grow a little over a run)
+        res["roofline"]["traffic"] = rec["hbm_bytes_per_call"]
+        res["roofline"]["traffic_over_algorithmic"] = rec["ratio_to_algorithmic"]
+        res["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
         res["cpu_baseline"] = cpu_baseline(cfg)

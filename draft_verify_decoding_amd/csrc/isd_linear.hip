@@ -22,6 +22,7 @@
 namespace isd {
 
 constexpr int kBK = 64;
+constexpr int kXcds = 8;  // XCDs of an MI355X
 constexpr int kLdsStride = kBK + 8;  // elements per LDS row
 
 struct GemmParams {
@@ -47,7 +48,18 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   const int wave = tid / kWave, lane = tid % kWave;
   const int lane32 = lane & 31, hh = lane >> 5;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-  const int m_blk = blockIdx.y * BM, n_blk = blockIdx.x * BN;
+  // Workgroups reach the XCDs round robin (workgroup id mod 8). Each XCD
+  // gets one contiguous run of tiles, M fastest, so a column block of W is
+  // fetched into a single XCD's L2 and read from HBM about once.
+  int m_blk, n_blk;
+  {
+    const int T = gridDim.x, nY = (p.M + BM - 1) / BM;
+    const int q = T / kXcds, rem = T % kXcds;
+    const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    const int t = xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
+    m_blk = (t % nY) * BM;
+    n_blk = (t / nY) * BN;
+  }
 
   // Global->register staging: thread loads rows (tid / 8) + 32*q, 16 bytes at
   // column 8 * (tid % 8) of the 64-wide K slab. A ring of DEPTH register
@@ -252,15 +264,13 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   const long cus = isd_device_cus_internal();
   const long big = static_cast<long>((p.M + 127) / 128) * ((cols + 127) / 128);
   const long small = static_cast<long>((p.M + 63) / 64) * ((cols + 63) / 64);
+  auto tiles = [&](int bm, int bn) { return dim3(static_cast<unsigned>(((p.M + bm - 1) / bm) * ((cols + bn - 1) / bn))); };
   if (big >= cus) {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth>), dim3((cols + 127) / 128, (p.M + 127) / 128), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth>), tiles(128, 128), dim3(256), 0, stream, p);
   } else if (small <= cus || small % cus == 0) {
-    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth>), dim3((cols + 63) / 64, (p.M + 63) / 64), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth>), tiles(64, 64), dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth>), dim3((cols + 63) / 64, (p.M + 127) / 128), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth>), tiles(128, 64), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
