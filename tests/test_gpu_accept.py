@@ -285,3 +285,67 @@ def test_same_inputs_same_bits():
     for k in ("accepted", "emit", "row_m", "row_s", "p_x", "resid_mass"):
         assert torch.equal(getattr(x, k).view(torch.int32), getattr(y, k).view(torch.int32)), k
     assert torch.equal(st_b.q_x, st_c.q_x) and torch.equal(st_b.drafts, st_c.drafts)
+
+
+def test_8b_single_sequence_full_vocab():
+    """C=1, N=4, bf16 logits N(0, 3^2) over 151,936 ids at context 4096,
+    draft noise for a mean acceptance of 0.9; 12 steps from FRESH."""
+    t, _ = run_trajectory(12, seed=2, C=1, N=4, V=151936, sigma_l=3.0,
+                          sigma_q=workload.SIGMA_Q_V151936[0.9], dtype=torch.bfloat16, ctx0=4096)
+    assert t.compared >= 11 and t.excused <= 1
+
+
+@pytest.mark.parametrize("p", [0.5, 0.7, 0.9])
+@pytest.mark.parametrize("N", [2, 3, 4, 6, 8])
+def test_stride_sweep_tokens_per_forward(N, p):
+    """32B-class sweep cell: C=16 sequences, vocab 151,936, 256 steps on the
+    device with draft noise calibrated for acceptance p. Two checks against
+    what the pages and the oracle fix:
+    - the measured per-draft acceptance equals sum_x min(P, Q) of the noise
+      model (calibrated with the oracle softmax, tests/golden/noise_sigma.json);
+    - tokens per forward equals the pages' closed form at that acceptance
+      (I-DLM, "Speedup Factor Explorer"), within 4 standard errors over the
+      16 independent sequences."""
+    import json
+    import os
+    from oracle import chain
+
+    C, V, steps, seed = 16, 151936, 256, 40 + N
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "noise_sigma.json")))
+    p_model = golden["check"][str(p)]
+    print(f"stride sweep N={N} p={p} C={C} steps={steps}", flush=True)
+    gen = workload.TeacherLogits(seed, C, V, steps * N + 2 * N + 1, 3.0, workload.SIGMA_Q_V151936[p],
+                                 torch.bfloat16, DEV)
+    ctx0 = torch.full((C,), 16384, dtype=torch.int64, device=DEV)
+    ctx = ctx0.clone()
+    s_in, s_out = dvd.SeqState(C, N), dvd.SeqState(C, N)
+    ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, 2 * N), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    prev = None
+    tokens = torch.zeros(C, dtype=torch.int64, device=DEV)
+    tests = torch.zeros(C, dtype=torch.int64, device=DEV)
+    passes = torch.zeros(C, dtype=torch.int64, device=DEV)
+    for t in range(steps):
+        n = s_in.n_draft.long()
+        lg = gen.block(t, ctx, ctx0, n, 2 * N)
+        out = dvd.isd_accept(lg, prev, s_in, s_out, N, seed, t, ws=ws, dev_err=err)
+        a = out.accepted.long()
+        tokens += out.n_emit.long()
+        tests += torch.where(n > 0, torch.minimum(a + 1, n), torch.zeros_like(n))
+        passes += a
+        ctx += out.kv_commit.long()
+        prev = lg
+        s_in, s_out = s_out, s_in
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    tpf_b = tokens.cpu().numpy() / steps
+    p_hat_b = passes.cpu().numpy() / np.maximum(tests.cpu().numpy(), 1)
+    tpf, se = tpf_b.mean(), tpf_b.std(ddof=1) / np.sqrt(C)
+    p_hat = passes.sum().item() / tests.sum().item()
+    p_se = p_hat_b.std(ddof=1) / np.sqrt(C)
+    closed = chain.tpf_closed_form(N, p_hat)
+    print(f"N={N} p={p}: acceptance {p_hat:.4f} +- {p_se:.4f} (noise model {p_model}); "
+          f"TPF {tpf:.4f} +- {se:.4f}, closed form at that acceptance {closed:.4f}, "
+          f"at the model's {chain.tpf_closed_form(N, p_model):.4f}", flush=True)
+    assert abs(p_hat - p_model) <= 4 * p_se + 0.01
+    assert abs(tpf - closed) <= 4 * se + 0.01

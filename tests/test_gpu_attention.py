@@ -153,3 +153,19 @@ def test_bad_page_id_sets_device_flag():
     dvd.isd_attention(kv, case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV), max_len=48, dev_err=err)
     torch.cuda.synchronize()
     assert err.item() & dvd.DEV_PAGE_OOB
+
+
+def test_8b_single_sequence_context_4096():
+    """C=1, N=4, 32/8 heads, D=128, 4096 cached tokens: every output checked."""
+    case = workload.AttentionCase(2, C=1, rows=8, Hq=32, Hkv=8, D=128, ctx=4096)
+    got, want = run(case)
+    assert slab_errors(got, want).max() < 2e-3
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 6, 8])
+def test_32b_stride_sweep_shapes(N):
+    """C=16, 64/8 heads, D=128, contexts of 16,384 tokens, block of 2N rows:
+    the whole batch runs, two sequences are checked in full."""
+    case = workload.AttentionCase(50 + N, C=16, rows=2 * N, Hq=64, Hkv=8, D=128, ctx=16384)
+    got, want = run(case, seqs=np.array([3, 12]))
+    assert slab_errors(got, want).max() < 2e-3
