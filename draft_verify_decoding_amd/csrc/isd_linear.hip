@@ -4,7 +4,8 @@
 // base model's outputs bit for bit (I-DLM, fr.news.hada.io, "Speedup Factor
 // Explorer" and "Documentation et ressources > Lossless R-ISD"). Here that
 // means: y = x W^T on every row with one fixed MFMA reduction order; MASK rows
-// then get y += s * (x A^T) B^T and clean rows are never written again.
+// then get y + s * (x A^T) B^T, and clean rows keep the base value itself
+// (selected, never recomputed).
 //
 // GEMM: y[M][Nout] fp32 = x[M][K] bf16 . W[Nout][K]^T bf16 ("NT": both
 // operands K-contiguous). Workgroup tile 2*WM x 2*WN (four waves, each WM x WN
@@ -12,11 +13,14 @@
 // padded rows (72 elements) so the 16-byte operand reads are conflict-free,
 // several slabs in flight in a register ring. The per-output reduction order
 // is slab by slab in ascending K and does not depend on M, the tile choice,
-// the other rows or the mask.
-// LoRA: U = x A^T comes out of the same GEMM as r extra output columns (A's
-// rows appended to W's); delta = U B^T then runs on bf16 MFMA with U split
-// into bf16 high and low halves (about 16 mantissa bits), and is added with
-// one fma to MASK rows only.
+// the other rows or the mask. A split-K launch runs the same loop over a
+// fixed share of the slabs (the split count depends only on K).
+// LoRA: U = x A^T first, as a split-K GEMM whose partials are summed in
+// split order. The delta U B^T of a 32x32 output block then runs on bf16
+// MFMA with U split into bf16 high and low halves (about 16 mantissa bits):
+// in the GEMM's epilogue for isd_linear_gated, in its own kernel for
+// gated_lora_apply, with the same instruction sequence, so the two give the
+// same bits.
 #include "isd_common.hpp"
 
 namespace isd {
@@ -25,16 +29,68 @@ constexpr int kBK = 64;
 constexpr int kXcds = 8;  // XCDs of an MI355X
 constexpr int kLdsStride = kBK + 8;  // elements per LDS row
 
+constexpr int kMaxSplits = 8;  // split-K shares of U = x A^T
+
+// Delta of LoRA rows on the 32x32 output block at (m0, n0): rows of U (fp32
+// [M][r]) against rows of B (bf16 [Nout][r]), r = 16 * R16. Register e of
+// lane (j, hh) is row m0 + 8(e/4) + 4hh + e%4, column n0 + j. Rows and
+// columns past the end contribute zeros.
+template <int R16>
+__device__ __forceinline__ f32x16 lora_delta_block(const float* U, const uint16_t* B, int M, int Nout, int m0,
+                                                   int n0, int lane32, int hh) {
+  constexpr int r = 16 * R16;
+  const int arow = m0 + lane32, bcol = n0 + lane32;
+  f32x4 uv[R16][2];
+  u32x4 bv[R16];
+#pragma unroll
+  for (int k = 0; k < R16; ++k) {
+    if (arow < M) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(U + static_cast<long>(arow) * r + 16 * k + 8 * hh);
+      uv[k][0] = src[0];
+      uv[k][1] = src[1];
+    } else {
+      uv[k][0] = uv[k][1] = f32x4{};
+    }
+    bv[k] = bcol < Nout ? *reinterpret_cast<const u32x4*>(B + static_cast<long>(bcol) * r + 16 * k + 8 * hh)
+                        : u32x4{0, 0, 0, 0};
+  }
+  // two independent MFMA chains (high and low halves), added at the end
+  f32x16 dh = {}, dl = {};
+#pragma unroll
+  for (int k = 0; k < R16; ++k) {
+    const float f[8] = {uv[k][0][0], uv[k][0][1], uv[k][0][2], uv[k][0][3],
+                        uv[k][1][0], uv[k][1][1], uv[k][1][2], uv[k][1][3]};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t ua = __float_as_uint(f[2 * t]) & 0xffff0000u, ub = __float_as_uint(f[2 * t + 1]) & 0xffff0000u;
+      hi[t] = (ua >> 16) | ub;
+      lo[t] = f32_to_bf16_bits(f[2 * t] - __uint_as_float(ua)) |
+              (f32_to_bf16_bits(f[2 * t + 1] - __uint_as_float(ub)) << 16);
+    }
+    const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[k]);
+    dh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi), bb, dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo), bb, dl, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dh[e] += dl[e];
+  return dh;
+}
+
 struct GemmParams {
-  const uint16_t* x;  // [M][K]
-  const uint16_t* w;  // [Nout][K]
-  const uint16_t* a;  // optional [r][K]: output columns Nout..Nout+r-1 use A's rows
-  float* y;           // [M][Nout]
-  float* u;           // [M][r] receives x A^T when a != nullptr
-  int M, K, Nout, r;
+  const uint16_t* x;    // [M][K]
+  const uint16_t* w;    // [Nout][K]
+  float* y;             // [splits][M][Nout]
+  // gated epilogue (R16 > 0): MASK rows get y = acc + scale * U B^T
+  const float* u;       // [M][r] fp32
+  const uint16_t* b;    // [Nout][r]
+  const uint8_t* mask;  // [M]
+  float scale;
+  int M, K, Nout;
+  int splits;           // K shares; split s runs slabs [s nk / splits, (s+1) nk / splits)
 };
 
-template <int WM, int WN, int DEPTH>
+template <int WM, int WN, int DEPTH, int R16>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   constexpr int BM = 2 * WM, BN = 2 * WN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -51,14 +107,16 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   // Workgroups reach the XCDs round robin (workgroup id mod 8). Each XCD
   // gets one contiguous run of tiles, M fastest, so a column block of W is
   // fetched into a single XCD's L2 and read from HBM about once.
-  int m_blk, n_blk;
+  int m_blk, n_blk, split;
   {
     const int T = gridDim.x, nY = (p.M + BM - 1) / BM;
     const int q = T / kXcds, rem = T % kXcds;
     const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
     const int t = xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
-    m_blk = (t % nY) * BM;
-    n_blk = (t / nY) * BN;
+    const int tiles = T / p.splits;
+    split = t / tiles;
+    m_blk = (t % tiles % nY) * BM;
+    n_blk = (t % tiles / nY) * BN;
   }
 
   // Global->register staging: thread loads rows (tid / 8) + 32*q, 16 bytes at
@@ -75,11 +133,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   for (int q = 0; q < A_ROUNDS; ++q)
     a_src[q] = p.x + static_cast<long>(min(m_blk + ld_row + 32 * q, p.M - 1)) * p.K + ld_col;
 #pragma unroll
-  for (int q = 0; q < B_ROUNDS; ++q) {
-    const int row = min(n_blk + ld_row + 32 * q, p.Nout + p.r - 1);
-    b_src[q] = (row < p.Nout ? p.w + static_cast<long>(row) * p.K : p.a + static_cast<long>(row - p.Nout) * p.K) +
-               ld_col;
-  }
+  for (int q = 0; q < B_ROUNDS; ++q)
+    b_src[q] = p.w + static_cast<long>(min(n_blk + ld_row + 32 * q, p.Nout - 1)) * p.K + ld_col;
   u32x4 ra[DEPTH][A_ROUNDS], rb[DEPTH][B_ROUNDS];
   auto load_slab = [&](int k0, u32x4 (&a)[A_ROUNDS], u32x4 (&b)[B_ROUNDS]) {
 #pragma unroll
@@ -123,9 +178,10 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 
   // Slabs past the last are clamped to it: their loads and the final LDS
   // store are harmless repeats whose data is never read.
-  const int nk = p.K / kBK;
+  const int nk_all = p.K / kBK;
+  const int kb = split * nk_all / p.splits, nk = (split + 1) * nk_all / p.splits - kb;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_slab(min(d, nk - 1) * kBK, ra[d], rb[d]);
+  for (int d = 0; d < DEPTH; ++d) load_slab((kb + min(d, nk - 1)) * kBK, ra[d], rb[d]);
   store_slab(0, ra[0], rb[0]);
   __syncthreads();
   for (int kt0 = 0; kt0 < nk; kt0 += DEPTH) {
@@ -138,48 +194,51 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
       // readers passed the previous barrier; ring slot d, whose slab is
       // already in LDS, is refilled with slab kt+DEPTH
       store_slab((kt + 1) & 1, ra[(d + 1) % DEPTH], rb[(d + 1) % DEPTH]);
-      load_slab(min(kt + DEPTH, nk - 1) * kBK, ra[d], rb[d]);
+      load_slab((kb + min(kt + DEPTH, nk - 1)) * kBK, ra[d], rb[d]);
       __syncthreads();
     }
   }
 
   // Epilogue: register e of lane (j, hh) is row 8(e/4) + 4hh + e%4 of the
-  // 32x32 block, column j; columns past Nout are the U = x A^T columns.
+  // 32x32 block, column j. Gated: a MASK row takes acc + scale * delta, a
+  // clean row takes acc itself.
+  float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int m0 = m_blk + wm + 32 * i, n0 = n_blk + wn + 32 * j;
       const int col = n0 + lane32;
+      f32x16 dl = {};
+      int live = 0;
+      if constexpr (R16 > 0) {
+        const int mine = m0 + lane32 < p.M ? p.mask[m0 + lane32] != 0 : 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) live |= __shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) << e;
+        if (__any(live)) dl = lora_delta_block<R16>(p.u, p.b, p.M, p.Nout, m0, n0, lane32, hh);
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (row >= p.M) continue;
-        if (col < p.Nout)
-          p.y[static_cast<long>(row) * p.Nout + col] = acc[i][j][e];
-        else if (col < p.Nout + p.r)
-          p.u[static_cast<long>(row) * p.r + (col - p.Nout)] = acc[i][j][e];
+        if (row < p.M && col < p.Nout)
+          y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[i][j][e]) : acc[i][j][e];
       }
     }
 }
 
 // y[m] += scale * (U B^T)[m] on MASK rows only, one wave per 32x32 tile of
-// y; tiles without a MASK row are skipped. U (fp32) is split into bf16 high
-// and low halves, so the product runs on bf16 MFMA (32x32x16) with both
-// operands read as 16-byte runs. Every load of a wave (its mask bytes, all of
-// U and B for the tile, then y of its MASK rows) is issued before the first
-// MFMA, so a tile costs about two memory round trips. Clean rows are never
-// written.
+// y; tiles without a MASK row are skipped and clean rows are never written.
+// The delta is the GEMM epilogue's, instruction for instruction.
 struct DeltaParams {
   const float* u;      // [M][r]
   const uint16_t* b;   // [Nout][r]
   const uint8_t* mask; // [M]
   float* y;            // [M][Nout]
-  int M, Nout, r;
+  int M, Nout;
   float scale;
 };
 
-template <int R16>  // r / 16
+template <int R16>
 __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lane32 = lane & 31, hh = lane >> 5;
@@ -187,60 +246,36 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
   const long tile = static_cast<long>(blockIdx.x) * 4 + wave;
   if (tile >= static_cast<long>((p.M + 31) / 32) * tiles_n) return;
   const int m0 = static_cast<int>(tile / tiles_n) * 32, n0 = static_cast<int>(tile % tiles_n) * 32;
-  const int arow = m0 + lane32, bcol = n0 + lane32;
-  const int mine = arow < p.M ? p.mask[arow] != 0 : 0;
-  if (!__any(mine)) return;
-
-  f32x4 uv[R16][2];
-  u32x4 bv[R16];
-#pragma unroll
-  for (int k = 0; k < R16; ++k) {
-    if (arow < p.M) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(p.u + static_cast<long>(arow) * p.r + 16 * k + 8 * hh);
-      uv[k][0] = src[0];
-      uv[k][1] = src[1];
-    } else {
-      uv[k][0] = uv[k][1] = f32x4{};
-    }
-    bv[k] = bcol < p.Nout ? *reinterpret_cast<const u32x4*>(p.b + static_cast<long>(bcol) * p.r + 16 * k + 8 * hh)
-                          : u32x4{0, 0, 0, 0};
-  }
-  // register e holds row 8(e/4) + 4hh + e%4 of the tile; its mask bit sits
-  // in the lane whose U row that is
-  float yv[16];
+  const int bcol = n0 + lane32;
+  const int mine = m0 + lane32 < p.M ? p.mask[m0 + lane32] != 0 : 0;
   int live = 0;
 #pragma unroll
+  for (int e = 0; e < 16; ++e) live |= (__shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) && bcol < p.Nout) << e;
+  if (!__any(live)) return;
+  // y of the MASK rows is loaded before the delta's operands arrive
+  float yv[16];
+#pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int rl = 8 * (e >> 2) + 4 * hh + (e & 3);
-    const int on = __shfl(mine, rl) && bcol < p.Nout;
-    live |= on << e;
-    yv[e] = on ? p.y[static_cast<long>(m0 + rl) * p.Nout + bcol] : 0.f;
+    const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+    yv[e] = ((live >> e) & 1) ? p.y[static_cast<long>(row) * p.Nout + bcol] : 0.f;
   }
-
-  f32x16 dl = {};
-#pragma unroll
-  for (int k = 0; k < R16; ++k) {
-    const float f[8] = {uv[k][0][0], uv[k][0][1], uv[k][0][2], uv[k][0][3],
-                        uv[k][1][0], uv[k][1][1], uv[k][1][2], uv[k][1][3]};
-    u32x4 hi, lo;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t ua = __float_as_uint(f[2 * t]) & 0xffff0000u, ub = __float_as_uint(f[2 * t + 1]) & 0xffff0000u;
-      hi[t] = (ua >> 16) | ub;
-      lo[t] = f32_to_bf16_bits(f[2 * t] - __uint_as_float(ua)) |
-              (f32_to_bf16_bits(f[2 * t + 1] - __uint_as_float(ub)) << 16);
-    }
-    const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[k]);
-    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi), bb, dl, 0, 0, 0);
-    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo), bb, dl, 0, 0, 0);
-  }
+  const f32x16 dl = lora_delta_block<R16>(p.u, p.b, p.M, p.Nout, m0, n0, lane32, hh);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if ((live >> e) & 1) {
-      const int rl = 8 * (e >> 2) + 4 * hh + (e & 3);
-      p.y[static_cast<long>(m0 + rl) * p.Nout + bcol] = fmaf(p.scale, dl[e], yv[e]);
+      const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+      p.y[static_cast<long>(row) * p.Nout + bcol] = fmaf(p.scale, dl[e], yv[e]);
     }
   }
+}
+
+// U = sum of the split-K partials of x A^T, in split order.
+__global__ __launch_bounds__(256) void lora_u_reduce_kernel(const float* part, float* U, long n, int splits) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int k = 1; k < splits; ++k) s += part[static_cast<long>(k) * n + i];
+  U[i] = s;
 }
 
 }  // namespace isd
@@ -251,28 +286,77 @@ using namespace isd;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Tile choice depends only on (M, output columns) and the CU count, never on
-// the data, and every choice gives each output the same reduction order.
+// Tile choice depends only on (M, Nout) and the CU count, never on the
+// data, and every choice gives each output the same reduction order.
 // 128x128 when that still gives one workgroup per CU. Otherwise 64x64 when
 // its workgroups spread evenly over the CUs (or fit in one round), else
 // 128x64: a CU that holds one 64x64 workgroup more than the others sets the
 // pace, because four resident 64x64 workgroups saturate its LDS bandwidth.
 constexpr int kDepth = 3;  // K slabs in flight per thread
 
-hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
-  const int cols = p.Nout + (p.a ? p.r : 0);
+template <int R16>
+hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   const long cus = isd_device_cus_internal();
-  const long big = static_cast<long>((p.M + 127) / 128) * ((cols + 127) / 128);
-  const long small = static_cast<long>((p.M + 63) / 64) * ((cols + 63) / 64);
-  auto tiles = [&](int bm, int bn) { return dim3(static_cast<unsigned>(((p.M + bm - 1) / bm) * ((cols + bn - 1) / bn))); };
-  if (big >= cus) {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth>), tiles(128, 128), dim3(256), 0, stream, p);
-  } else if (small <= cus || small % cus == 0) {
-    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth>), tiles(64, 64), dim3(256), 0, stream, p);
+  auto tiles = [&](int bm, int bn) { return static_cast<long>((p.M + bm - 1) / bm) * ((p.Nout + bn - 1) / bn); };
+  const long big = tiles(128, 128), small = tiles(64, 64);
+  auto grid = [&](long t) { return dim3(static_cast<unsigned>(t * p.splits)); };
+  if (p.splits == 1 && big >= cus) {
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth, R16>), grid(big), dim3(256), 0, stream, p);
+  } else if (p.splits > 1 || small <= cus || small % cus == 0) {
+    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth, R16>), grid(small), dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth>), tiles(128, 64), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth, R16>), grid(tiles(128, 64)), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmParams& p, int r, hipStream_t stream) {
+  switch (r / 16) {
+    case 0: return launch_gemm_r<0>(p, stream);
+    case 1: return launch_gemm_r<1>(p, stream);
+    case 2: return launch_gemm_r<2>(p, stream);
+    case 3: return launch_gemm_r<3>(p, stream);
+    case 4: return launch_gemm_r<4>(p, stream);
+    case 5: return launch_gemm_r<5>(p, stream);
+    case 6: return launch_gemm_r<6>(p, stream);
+    case 7: return launch_gemm_r<7>(p, stream);
+    default: return launch_gemm_r<8>(p, stream);
+  }
+}
+
+// Split count of U = x A^T: a function of K only (so U's bits do not depend
+// on M), the largest of 8, 4, 2, 1 that divides the slab count.
+int u_splits(int K) {
+  const int nk = K / kBK;
+  int s = kMaxSplits;
+  while (s > 1 && nk % s != 0) s /= 2;
+  return s;
+}
+
+size_t part_bytes(int M, int r) { return (static_cast<size_t>(M) * r * sizeof(float) * kMaxSplits + 255) & ~static_cast<size_t>(255); }
+
+// U = x A^T into the workspace: split-K partials, then their sum.
+hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
+  float* part = static_cast<float*>(ws);
+  float* U = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(M, r));
+  GemmParams g{};
+  g.x = static_cast<const uint16_t*>(x);
+  g.w = static_cast<const uint16_t*>(A);
+  g.y = part;
+  g.M = M;
+  g.K = K;
+  g.Nout = r;
+  g.splits = u_splits(K);
+  hipError_t e = launch_gemm_r<0>(g, stream);
+  if (e != hipSuccess) return e;
+  const long n = static_cast<long>(M) * r;
+  hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, part,
+                     U, n, g.splits);
+  return hipGetLastError();
+}
+
+const float* lora_u_of(void* ws, int M, int r) {
+  return reinterpret_cast<const float*>(static_cast<char*>(ws) + part_bytes(M, r));
 }
 
 hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int M, int Nout, int r, float scale,
@@ -284,7 +368,6 @@ hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int 
   d.y = y;
   d.M = M;
   d.Nout = Nout;
-  d.r = r;
   d.scale = scale;
   const long tiles = static_cast<long>((M + 31) / 32) * ((Nout + 31) / 32);
   const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
@@ -314,8 +397,7 @@ int check_lora_args(const void* A, const void* B, const uint8_t* mask, int r, vo
   if (!A || !B || !mask) return ISD_E_INVALID;
   if (r < 16 || r > 128 || r % 16 != 0) return ISD_E_UNSUPPORTED;
   if (!aligned16(A) || !aligned16(B)) return ISD_E_INVALID;
-  const size_t need = static_cast<size_t>(M) * r * sizeof(float);
-  if (!ws || ws_bytes < need || !aligned16(ws)) return ISD_E_WORKSPACE;
+  if (!ws || ws_bytes < isd_lora_workspace_size(M, r) || !aligned16(ws)) return ISD_E_WORKSPACE;
   return ISD_OK;
 }
 
@@ -335,12 +417,13 @@ int isd_linear(const void* x, const void* W, int M, int K, int Nout, float* y, h
   p.M = M;
   p.K = K;
   p.Nout = Nout;
-  return launch_gemm(p, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+  p.splits = 1;
+  return launch_gemm(p, 0, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
 size_t isd_lora_workspace_size(int M, int r) {
   if (M < 0 || r < 0) return 0;
-  return static_cast<size_t>(M) * r * sizeof(float);
+  return part_bytes(M, r) + static_cast<size_t>(M) * r * sizeof(float);
 }
 
 int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t* is_mask, int M, int K, int Nout,
@@ -351,19 +434,9 @@ int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t*
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  // U = x A^T through the projection GEMM (A's rows as the output columns),
-  // so U is bit-identical to the U columns of the fused call below.
-  GemmParams p{};
-  p.x = static_cast<const uint16_t*>(x);
-  p.w = static_cast<const uint16_t*>(A);
-  p.y = static_cast<float*>(ws);
-  p.M = M;
-  p.K = K;
-  p.Nout = r;
-  if (launch_gemm(p, stream) != hipSuccess) return ISD_E_LAUNCH;
-  return launch_delta(static_cast<const float*>(ws), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess
-             ? ISD_OK
-             : ISD_E_LAUNCH;
+  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
+  return launch_delta(lora_u_of(ws, M, r), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess ? ISD_OK
+                                                                                                   : ISD_E_LAUNCH;
 }
 
 int isd_linear_gated(const void* x, const void* W, const void* A, const void* B, const uint8_t* is_mask, int M, int K,
@@ -374,20 +447,20 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
+  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
-  p.a = static_cast<const uint16_t*>(A);
   p.y = y;
-  p.u = static_cast<float*>(ws);
+  p.u = lora_u_of(ws, M, r);
+  p.b = static_cast<const uint16_t*>(B);
+  p.mask = is_mask;
+  p.scale = scale;
   p.M = M;
   p.K = K;
   p.Nout = Nout;
-  p.r = r;
-  if (launch_gemm(p, stream) != hipSuccess) return ISD_E_LAUNCH;
-  return launch_delta(static_cast<const float*>(ws), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess
-             ? ISD_OK
-             : ISD_E_LAUNCH;
+  p.splits = 1;
+  return launch_gemm(p, r, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
 }  // extern "C"

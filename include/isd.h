@@ -211,13 +211,13 @@ int isd_accept(const isd_accept_args* args, hipStream_t stream);
  * rows or on their mask.
  * gated_lora_apply: y[m] += scale * (x[m] A^T) B^T for rows with
  * is_mask[m] != 0; A [r][K] and B [Nout][r] bf16; other rows are never
- * written. U = x A^T (fp32) lands in the workspace, which must hold
- * isd_lora_workspace_size(M, r) = M * r * 4 bytes (16-byte aligned, owned by
- * the caller, contents on entry ignored, U on return).
- * isd_linear_gated: y = isd_linear(x, W) then gated_lora_apply, with U
- * computed inside the base GEMM as r extra output columns; its clean rows
- * equal isd_linear's bit for bit and its MASK rows equal those of the two
- * separate calls.
+ * written. U = x A^T (fp32, a split-K GEMM whose split count depends on K
+ * only) is built in the workspace, which must hold
+ * isd_lora_workspace_size(M, r) bytes (16-byte aligned, owned by the caller,
+ * contents on entry ignored).
+ * isd_linear_gated: y = isd_linear(x, W) then gated_lora_apply, with the
+ * delta added in the base GEMM's epilogue; its clean rows equal isd_linear's
+ * bit for bit and its MASK rows equal those of the two separate calls.
  * x, W, A, B must be 16-byte aligned, all row-major and contiguous.
  * Supported: K multiple of 64; r multiple of 16, <= 128. M == 0 or Nout == 0
  * returns ISD_OK with nothing launched. Errors: ISD_E_INVALID (null or

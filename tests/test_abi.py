@@ -110,5 +110,5 @@ def test_linear_rejects_bad_arguments_on_host(lib):
     assert lib.isd_linear(16, 16, 0, 64, 8, 16, None) == 0  # empty problem
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, 16, 1 << 20, None) == -2  # rank 24
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 16, 8, None) == -3  # ws too small
-    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4  # U = x A^T in fp32
+    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4 * 9  # 8 split-K partials of U, then U
     assert lib.gated_lora_apply(16, 16, 24, 16, 4, 64, 8, 32, 1.0, 16, 16, 512, None) == -1  # B misaligned
