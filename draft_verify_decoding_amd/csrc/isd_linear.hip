@@ -8,13 +8,14 @@
 // (selected, never recomputed).
 //
 // GEMM: y[M][Nout] fp32 = x[M][K] bf16 . W[Nout][K]^T bf16 ("NT": both
-// operands K-contiguous). Workgroup tile 2*WM x 2*WN (four waves, each WM x WN
-// in 32x32 MFMA blocks), K in slabs of 64 through double-buffered LDS with
-// padded rows (72 elements) so the 16-byte operand reads are conflict-free,
-// several slabs in flight in a register ring. The per-output reduction order
-// is slab by slab in ascending K and does not depend on M, the tile choice,
-// the other rows or the mask. A split-K launch runs the same loop over a
-// fixed share of the slabs (the split count depends only on K).
+// operands K-contiguous). Four waves in a 2 x 2 grid, each TM x TN blocks of
+// 32 x 32 (v_mfma_f32_32x32x16_bf16). K advances in slabs of 64 that travel
+// from global memory straight into LDS (16-byte direct loads, XOR-swizzled
+// rows, no register staging), three or four stages deep with one barrier per
+// slab. The per-output reduction order is slab by slab in ascending K and
+// does not depend on M, the tile choice, the other rows or the mask. A
+// split-K launch runs the same loop over a fixed share of the slabs (the
+// split count depends only on K).
 // LoRA: U = x A^T first, as a split-K GEMM whose partials are summed in
 // split order. The delta U B^T of a 32x32 output block then runs on bf16
 // MFMA with U split into bf16 high and low halves (about 16 mantissa bits):
@@ -27,7 +28,6 @@ namespace isd {
 
 constexpr int kBK = 64;
 constexpr int kXcds = 8;  // XCDs of an MI355X
-constexpr int kLdsStride = kBK + 8;  // elements per LDS row
 
 constexpr int kMaxSplits = 8;  // split-K shares of U = x A^T
 
@@ -90,15 +90,47 @@ struct GemmParams {
   int splits;           // K shares; split s runs slabs [s nk / splits, (s+1) nk / splits)
 };
 
-template <int WM, int WN, int DEPTH, int R16>
+// Wait until at most n vector-memory operations of this wave are in flight
+// and all of its LDS operations are done (exp counter not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// would wait for every direct load in flight); the waits the loop needs are
+// explicit, and the empty asm keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes
+// land at dst + 16 i (dst is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// Four waves in a 2 x 2 grid, each computing TM x TN blocks of 32 x 32, so
+// a workgroup tile is 64 TM x 64 TN. Per 16-deep step a wave reads TM + TN
+// operand fragments (1 KB each) from LDS for TM * TN MFMAs: larger wave tiles
+// need less LDS bandwidth per MFMA, which is what bounds this loop.
+template <int TM, int TN, int STAGES, int R16>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
+  constexpr int WM = 32 * TM, WN = 32 * TN;
   constexpr int BM = 2 * WM, BN = 2 * WN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_ROUNDS = BM * kBK / 8 / 256;  // 16-byte loads per thread
-  constexpr int B_ROUNDS = BN * kBK / 8 / 256;
-  static_assert(A_ROUNDS >= 1 && B_ROUNDS >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kLdsStride];
+  constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;  // 1 KB direct loads per wave and slab
+  constexpr int STAGE = (BM + BN) * kBK;                // elements per stage
+  // one LDS object per stage, so the compiler can tell that reading a stage
+  // does not wait for the direct loads into the others
+  static_assert(STAGES == 3 || STAGES == 4, "three or four stages");
+  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGES == 4 ? STAGE : 8];
+  auto stage_ptr = [&](int stage) -> uint16_t* {
+    return stage == 0 ? st0 : (stage == 1 ? st1 : (stage == 2 ? st2 : st3));
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -119,36 +151,31 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     n_blk = (t % tiles / nY) * BN;
   }
 
-  // Global->register staging: thread loads rows (tid / 8) + 32*q, 16 bytes at
-  // column 8 * (tid % 8) of the 64-wide K slab. A ring of DEPTH register
-  // sets keeps DEPTH slabs in flight; LDS is double-buffered. Every load is
-  // unconditional (no divergent branch around it), so the compiler waits
-  // only for the slab it is about to store: rows past the end read the last
-  // valid row instead. Output row i depends only on A row i and column j only
-  // on B row j, and such rows and columns are never written.
-  const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
-  const uint16_t* a_src[A_ROUNDS];
-  const uint16_t* b_src[B_ROUNDS];
+  // Slabs go from global memory straight into LDS (16-byte direct loads, no
+  // register staging). A stage holds the slab's BM rows of x, then its BN rows
+  // of W, 128 bytes per row with the 16-byte chunks XOR-swizzled: chunk c of
+  // row r sits at slot c ^ (r % 8), so both the loads (lane i of a load
+  // fills slot i % 8 of row i / 8 of an 8-row group) and the MFMA operand
+  // reads (eight rows at one chunk) touch every bank once. Rows past the end
+  // read the last valid row: output row i depends only on A row i and column
+  // j only on B row j, and such rows and columns are never written.
+  const int g_row = lane >> 3, g_chunk = (lane & 7) ^ (lane >> 3);
+  const uint16_t* a_src[A_LOADS];
+  const uint16_t* b_src[B_LOADS];
 #pragma unroll
-  for (int q = 0; q < A_ROUNDS; ++q)
-    a_src[q] = p.x + static_cast<long>(min(m_blk + ld_row + 32 * q, p.M - 1)) * p.K + ld_col;
+  for (int q = 0; q < A_LOADS; ++q)
+    a_src[q] = p.x + static_cast<long>(min(m_blk + 8 * (wave + 4 * q) + g_row, p.M - 1)) * p.K + 8 * g_chunk;
 #pragma unroll
-  for (int q = 0; q < B_ROUNDS; ++q)
-    b_src[q] = p.w + static_cast<long>(min(n_blk + ld_row + 32 * q, p.Nout - 1)) * p.K + ld_col;
-  u32x4 ra[DEPTH][A_ROUNDS], rb[DEPTH][B_ROUNDS];
-  auto load_slab = [&](int k0, u32x4 (&a)[A_ROUNDS], u32x4 (&b)[B_ROUNDS]) {
+  for (int q = 0; q < B_LOADS; ++q)
+    b_src[q] = p.w + static_cast<long>(min(n_blk + 8 * (wave + 4 * q) + g_row, p.Nout - 1)) * p.K + 8 * g_chunk;
+  auto load_slab = [&](int k0, int stage) {
+    uint16_t* base = stage_ptr(stage);
 #pragma unroll
-    for (int q = 0; q < A_ROUNDS; ++q) a[q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
+    for (int q = 0; q < A_LOADS; ++q)
+      load_lds16(a_src[q] + k0, base + 8 * (wave + 4 * q) * kBK);
 #pragma unroll
-    for (int q = 0; q < B_ROUNDS; ++q) b[q] = *reinterpret_cast<const u32x4*>(b_src[q] + k0);
-  };
-  auto store_slab = [&](int buf, const u32x4 (&a)[A_ROUNDS], const u32x4 (&b)[B_ROUNDS]) {
-#pragma unroll
-    for (int q = 0; q < A_ROUNDS; ++q)
-      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = a[q];
-#pragma unroll
-    for (int q = 0; q < B_ROUNDS; ++q)
-      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row + 32 * q) * kLdsStride + ld_col]) = b[q];
+    for (int q = 0; q < B_LOADS; ++q)
+      load_lds16(b_src[q] + k0, base + (BM + 8 * (wave + 4 * q)) * kBK);
   };
 
   f32x16 acc[TM][TN];
@@ -157,18 +184,20 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](int buf) {
+  const int sw = lane32 & 7;  // row % 8 of every operand row this lane reads
+  auto compute = [&](int stage) {
+    const uint16_t* sA = stage_ptr(stage);
+    const uint16_t* sB = sA + BM * kBK;
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
+      const int slot = ((2 * s + hh) ^ sw) * 8;
       bf16x8 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&sA[buf][(wm + 32 * i + lane32) * kLdsStride + 16 * s + 8 * hh]));
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sA[(wm + 32 * i + lane32) * kBK + slot]));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&sB[buf][(wn + 32 * j + lane32) * kLdsStride + 16 * s + 8 * hh]));
+        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sB[(wn + 32 * j + lane32) * kBK + slot]));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -176,28 +205,36 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     }
   };
 
-  // Slabs past the last are clamped to it: their loads and the final LDS
-  // store are harmless repeats whose data is never read.
+  // STAGES-1 slabs in flight ahead of the one being multiplied. Slabs past
+  // the last are clamped to it: their loads are harmless repeats into a stage
+  // that is never read again.
   const int nk_all = p.K / kBK;
   const int kb = split * nk_all / p.splits, nk = (split + 1) * nk_all / p.splits - kb;
+  constexpr int kLoads = A_LOADS + B_LOADS;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_slab((kb + min(d, nk - 1)) * kBK, ra[d], rb[d]);
-  store_slab(0, ra[0], rb[0]);
-  __syncthreads();
-  for (int kt0 = 0; kt0 < nk; kt0 += DEPTH) {
+  for (int d = 0; d < STAGES - 1; ++d) load_slab((kb + min(d, nk - 1)) * kBK, d);
+  // unrolled over kUnroll slabs: the compiler proves that reading one stage
+  // need not wait for the loads into the others only inside one trip of the
+  // loop, and waits for every load once per trip
+  constexpr int kUnroll = 4 * STAGES;
+  for (int kt0 = 0; kt0 < nk; kt0 += kUnroll) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int kt = kt0 + d;
+    for (int dd = 0; dd < kUnroll; ++dd) {
+      const int d = dd % STAGES;
+      const int kt = kt0 + dd;
       if (kt >= nk) break;
-      compute(kt & 1);
-      // slab kt+1 (in ring slot d+1) goes to the other LDS buffer, whose
-      // readers passed the previous barrier; ring slot d, whose slab is
-      // already in LDS, is refilled with slab kt+DEPTH
-      store_slab((kt + 1) & 1, ra[(d + 1) % DEPTH], rb[(d + 1) % DEPTH]);
-      load_slab((kb + min(kt + DEPTH, nk - 1)) * kBK, ra[d], rb[d]);
-      __syncthreads();
+      // this wave's loads of slab kt are done once only the STAGES-2 later
+      // slabs' loads may still be in flight, and its reads of slab kt-1's
+      // stage are done once no LDS operation is; after the barrier every
+      // wave's part of slab kt is in LDS and nobody reads the stage that the
+      // next load overwrites (slab kt-1's)
+      wait_vm_lgkm0<(STAGES - 2) * kLoads>();
+      stage_barrier();
+      load_slab((kb + min(kt + STAGES - 1, nk - 1)) * kBK, (d + STAGES - 1) % STAGES);
+      compute(d);
     }
   }
+  wait_vm_lgkm0<0>();
 
   // Epilogue: register e of lane (j, hh) is row 8(e/4) + 4hh + e%4 of the
   // 32x32 block, column j. Gated: a MASK row takes acc + scale * delta, a
@@ -287,27 +324,31 @@ using namespace isd;
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // Tile choice depends only on (M, Nout) and the CU count, never on the
-// data, and every choice gives each output the same reduction order.
-// 128x128 when that still gives one workgroup per CU. Otherwise 64x64 when
-// its workgroups spread evenly over the CUs (or fit in one round), else
-// 128x64: a CU that holds one 64x64 workgroup more than the others sets the
-// pace, because four resident 64x64 workgroups saturate its LDS bandwidth.
-constexpr int kDepth = 3;  // K slabs in flight per thread
+// data, and every choice gives each output the same reduction order. The
+// largest wave tile whose workgroups still cover every CU wins (fewer LDS
+// bytes per MFMA); those run one workgroup per CU with four LDS stages.
+// Otherwise 64 x 64 tiles, three stages, three workgroups per CU.
+template <int TM, int TN, int R16>
+hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
+  const long tiles = static_cast<long>((p.M + 64 * TM - 1) / (64 * TM)) * ((p.Nout + 64 * TN - 1) / (64 * TN));
+  constexpr int stages = (TM * TN > 1) ? 4 : 3;
+  hipLaunchKernelGGL((gemm_nt_kernel<TM, TN, stages, R16>), dim3(static_cast<unsigned>(tiles * p.splits)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 template <int R16>
 hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   const long cus = isd_device_cus_internal();
-  auto tiles = [&](int bm, int bn) { return static_cast<long>((p.M + bm - 1) / bm) * ((p.Nout + bn - 1) / bn); };
-  const long big = tiles(128, 128), small = tiles(64, 64);
-  auto grid = [&](long t) { return dim3(static_cast<unsigned>(t * p.splits)); };
-  if (p.splits == 1 && big >= cus) {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 64, kDepth, R16>), grid(big), dim3(256), 0, stream, p);
-  } else if (p.splits > 1 || small <= cus || small % cus == 0) {
-    hipLaunchKernelGGL((gemm_nt_kernel<32, 32, kDepth, R16>), grid(small), dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<64, 32, kDepth, R16>), grid(tiles(128, 64)), dim3(256), 0, stream, p);
+  auto tiles = [&](int tm, int tn) {
+    return static_cast<long>((p.M + 64 * tm - 1) / (64 * tm)) * ((p.Nout + 64 * tn - 1) / (64 * tn));
+  };
+  if (p.splits == 1) {
+    if (tiles(2, 2) >= cus) return launch_tile<2, 2, R16>(p, stream);
+    if (tiles(1, 3) >= cus) return launch_tile<1, 3, R16>(p, stream);
+    if (tiles(1, 2) >= cus) return launch_tile<1, 2, R16>(p, stream);
   }
-  return hipGetLastError();
+  return launch_tile<1, 1, R16>(p, stream);
 }
 
 hipError_t launch_gemm(const GemmParams& p, int r, hipStream_t stream) {
