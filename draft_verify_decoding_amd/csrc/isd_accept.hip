@@ -10,17 +10,19 @@
 // the FULL/FRESH alternation are what reproduce the page's tokens-per-forward
 // closed form ("Speedup Factor Explorer").
 //
-// Three launches, all HBM-streaming and deterministic:
+// Two launches, both HBM-streaming and deterministic:
 //   stats   one pass over every logits row the step may read: per 8192-entry
-//           chunk, the max and sum of exp(l - max) (fp32 from exact bf16).
+//           chunk, the max and sum of exp(l - max) (fp32 from exact bf16);
+//           a workgroup takes two chunks with all their loads in flight.
 //   sample  grid (slices, sequences). Every workgroup rebuilds the row
 //           statistics and the accept decision from the chunk stats (same
 //           fixed-order arithmetic, so all agree). On a rejection each slice
 //           sums the residual max(0, P_a - Q_{a+1}) over its chunk; when all
 //           drafts pass, slice k rescans the one chunk where the CDF of row
 //           n + k crosses its uniform (bonus for k = 0, proposals after).
-//   finish  one workgroup per sequence: residual chunk choice and rescan,
-//           outputs, next state.
+//           The last workgroup of a sequence to finish (a counter per
+//           sequence, zeroed by the stats launch) then picks and rescans the
+//           residual chunk and writes the outputs and the next state.
 #include "isd_common.hpp"
 
 namespace isd {
@@ -28,7 +30,9 @@ namespace isd {
 constexpr int kChunk = 8192;     // vocab entries per stats chunk
 constexpr int kThreads = 256;    // threads per workgroup
 constexpr int kPerThread = 32;   // entries per thread in a chunk
+constexpr int kStatsChunks = 2;  // chunks per workgroup of the stats launch
 constexpr int kMaxN = 8;
+constexpr int kMaxChunks = 64;   // vocabularies up to 524,288 entries
 static_assert(kThreads * kPerThread == kChunk, "chunk tiling");
 
 struct AcceptParams {
@@ -41,10 +45,33 @@ struct AcceptParams {
   int32_t *accepted, *n_emit, *emit, *kv_commit, *ctx;
   float *p_x, *resid_mass, *row_m, *row_s;
   float2* stats;    // [C][rows][nch] (chunk max, chunk sum)
-  float* resid;     // [C][ns] residual slice sums
+  float* resid;     // [C][nch] residual sum per chunk
   int2* samp;       // [C][N] (token, bits of q(x)) from the sample kernel
+  int* arrive;      // [C] workgroups of the sample launch done, per sequence
   int32_t* dev_err;
 };
+
+// ------------------------------------------- values handed between workgroups
+// The slice results of the sample launch reach the sequence's last
+// workgroup through device-coherent (agent-scope) atomic stores and loads,
+// so no cache-wide writeback or invalidate is needed: the writer waits for
+// its store to complete before it counts itself in.
+__device__ __forceinline__ void put_f32(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_f32(float* ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_sample(int2* ptr, int tok, float q) {
+  const unsigned long long v =
+      static_cast<unsigned long long>(static_cast<uint32_t>(tok)) | (static_cast<unsigned long long>(__float_as_uint(q)) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(ptr), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 get_sample(int2* ptr) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<unsigned long long*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_int2(static_cast<int>(static_cast<uint32_t>(v)), static_cast<int>(static_cast<uint32_t>(v >> 32)));
+}
 
 // ------------------------------------------------------------ Philox4x64-10
 // Salmon et al., SC'11: two 64x64->128 multiplies per round, Weyl key bumps,
@@ -175,86 +202,138 @@ __device__ __forceinline__ float block_exclusive_scan(float v) {
 }
 
 // ============================================================ stats kernel
+// Entries c*kChunk + i*2048 + 8t .. +7 (i = 0..3) of chunk c go to thread t:
+// each load instruction of the workgroup reads 4 KB of contiguous logits.
+// (A chunk's max and sum do not depend on which thread holds what; the
+// sampling rescans keep token order per thread.)
+template <typename E>
+__device__ __forceinline__ void load_chunk_coalesced(const E* row, int V, int c, float (&x)[kPerThread]) {
+  constexpr int KP = Elem<E>::kPerVec;  // 8 bf16 or 4 fp32 per 16 bytes
+#pragma unroll
+  for (int q = 0; q < kPerThread / KP; ++q) {
+    const int vq = c * kChunk + q * kThreads * KP + threadIdx.x * KP;
+    if (vq + KP <= V) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + vq);
+      float f[KP];
+      unpack16(w, f);
+#pragma unroll
+      for (int k = 0; k < KP; ++k) x[q * KP + k] = f[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) x[q * KP + k] = (vq + k < V) ? load_elem(row, vq + k) : -INFINITY;
+    }
+  }
+}
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
-  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int c0 = blockIdx.x * kStatsChunks, r = blockIdx.y, b = blockIdx.z;
+  if (c0 == 0 && r == 0 && threadIdx.x == 0) p.arrive[b] = 0;  // the sample launch counts from zero
   int n = p.in.n_draft[b];
   n = n < 0 ? 0 : (n > p.N - 1 ? p.N - 1 : n);
   if (r > n + p.N - 1) return;
-  float x[kPerThread];
-  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
-  float m = -INFINITY;
+  const E* row = row_ptr<E>(p.logits, p.ld, p.rows, b, r);
+  float x[kStatsChunks][kPerThread];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
-  float s = 0.f;
-  if (m != -INFINITY) {
-    const float ml = m * kLog2e;
+  for (int h = 0; h < kStatsChunks; ++h) {
+    if (c0 + h < p.nch) {
+      load_chunk_coalesced<E>(row, p.V, c0 + h, x[h]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) s += weight_of(x[k], ml);
+      for (int k = 0; k < kPerThread; ++k) x[h][k] = -INFINITY;
+    }
   }
-  block_reduce_ms(m, s);
-  if (threadIdx.x == 0) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c] = make_float2(m, s);
+#pragma unroll
+  for (int h = 0; h < kStatsChunks; ++h) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[h][k]);
+    float s = 0.f;
+    if (m != -INFINITY) {
+      const float ml = m * kLog2e;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) s += weight_of(x[h][k], ml);
+    }
+    block_reduce_ms(m, s);
+    if (threadIdx.x == 0 && c0 + h < p.nch) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c0 + h] = make_float2(m, s);
+  }
 }
 
 // ------------------------------------------------ shared per-sequence logic
 struct Decision {
-  int n, a, err;        // err: ISD_DEV_* bits, 0 if the step can be taken
-  float M[2 * kMaxN];   // row max
-  float S[2 * kMaxN];   // row sum exp(l - M)
-  float u[2 * kMaxN];   // uniforms by slot
-  float px[kMaxN];      // P_{j-1}(x_j) of tested drafts
+  int n, a, err;                     // err: ISD_DEV_* bits, 0 if the step can be taken
+  int qrow;                          // first row of the previous step that proposed
+  float M[2 * kMaxN];                // row max
+  float S[2 * kMaxN];                // row sum exp(l - M)
+  float u[2 * kMaxN];                // uniforms by slot
+  float px[kMaxN];                   // P_{j-1}(x_j) of tested drafts
+  float2 st[2 * kMaxN][kMaxChunks];  // chunk (max, sum) of the rows read
 };
 
 // Rebuild row statistics, uniforms and the accept decision of sequence b.
-// Every workgroup that calls this computes the same values. Result in LDS.
+// Every workgroup that calls this computes the same values. The state, the
+// chunk statistics of every row and the uniforms are fetched together; the
+// logits of the drafts follow in one more round trip. Result in LDS.
 template <typename E>
 __device__ void decide(const AcceptParams& p, int b, Decision& d) {
   const int tid = threadIdx.x;
+  const int N = p.N, nd = N - 1, R = 2 * N - 1;
+  __shared__ int s_n, s_draft[kMaxN];
+  __shared__ float s_qx[kMaxN], s_pall[kMaxN];
   if (tid == 0) {
-    int n = p.in.n_draft[b];
+    s_n = p.in.n_draft[b];
+    d.qrow = p.in.q_row[b];
+  }
+  if (tid < nd) {
+    s_draft[tid] = p.in.drafts[b * nd + tid];
+    s_qx[tid] = p.in.q_x[b * nd + tid];
+  }
+  for (int i = tid; i < R * p.nch; i += kThreads)
+    d.st[i / p.nch][i % p.nch] = p.stats[(static_cast<long>(b) * p.rows + i / p.nch) * p.nch + i % p.nch];
+  if (tid < 2 * N)
+    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), p.step, 0ull, p.seed, 0ull));
+  __syncthreads();
+  // every thread clamps n the same way; thread 0 records what was wrong
+  const int n_raw = s_n;
+  const int n = (n_raw < 0 || n_raw > nd) ? 0 : n_raw;
+  if (tid == 0) {
     int err = 0;
-    if (n < 0 || n > p.N - 1) {
-      err |= ISD_DEV_STATE;
-      n = 0;
-    }
-    if (n > 0 && (!p.prev_logits || p.in.q_row[b] < 0 || p.in.q_row[b] + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
-    for (int j = 0; j < n; ++j) {
-      const int x = p.in.drafts[b * (p.N - 1) + j];
-      if (x < 0 || x >= p.V) err |= ISD_DEV_TOKEN_OOB;
-    }
+    if (n_raw < 0 || n_raw > nd) err |= ISD_DEV_STATE;
+    if (n > 0 && (!p.prev_logits || d.qrow < 0 || d.qrow + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
+    for (int j = 0; j < n; ++j)
+      if (s_draft[j] < 0 || s_draft[j] >= p.V) err |= ISD_DEV_TOKEN_OOB;
     d.n = n;
     d.err = err;
   }
+  // the logit of draft j+1 in verify row j (loaded before the row sums exist)
+  float lx = 0.f;
+  const bool draft_ok = tid < n && s_draft[tid] >= 0 && s_draft[tid] < p.V;
+  if (draft_ok) lx = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, tid), s_draft[tid]);
+  const int nrows = n + N;  // rows 0 .. n + N - 1
   __syncthreads();
-  const int n = d.n;
-  const int nrows = n + p.N;  // rows 0 .. n + N - 1
   if (tid < nrows) {
-    const float2* st = p.stats + (static_cast<long>(b) * p.rows + tid) * p.nch;
     float M = -INFINITY;
-    for (int c = 0; c < p.nch; ++c) M = fmaxf(M, st[c].x);
+    for (int c = 0; c < p.nch; ++c) M = fmaxf(M, d.st[tid][c].x);
     float S = 0.f;
     if (M != -INFINITY) {
-      for (int c = 0; c < p.nch; ++c) S += st[c].y * fast_exp2((st[c].x - M) * kLog2e);
+      for (int c = 0; c < p.nch; ++c) S += d.st[tid][c].y * fast_exp2((d.st[tid][c].x - M) * kLog2e);
     }
     d.M[tid] = M;
     d.S[tid] = S;
     if (!(M > -INFINITY && M < INFINITY && S > 0.f && S < INFINITY)) atomicOr(&d.err, static_cast<int>(ISD_DEV_NONFINITE));
   }
-  if (tid < 2 * p.N)
-    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), p.step, 0ull, p.seed, 0ull));
+  __syncthreads();
+  if (tid < n) s_pall[tid] = draft_ok ? prob_of(lx, d.M[tid], d.S[tid]) : NAN;
   __syncthreads();
   if (tid == 0) {
     int a = 0;
     for (int j = 0; j < kMaxN; ++j) d.px[j] = NAN;
     if (!d.err) {
       for (int j = 1; j <= n; ++j) {
-        const int x = p.in.drafts[b * (p.N - 1) + j - 1];
-        const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, j - 1), x);
-        const float px = prob_of(l, d.M[j - 1], d.S[j - 1]);
-        const float qx = p.in.q_x[b * (p.N - 1) + j - 1];
+        const float px = s_pall[j - 1];
         d.px[j - 1] = px;
         // u * q < p compared exactly (fp32 operands, exact fp64 product).
-        if (static_cast<double>(d.u[j]) * static_cast<double>(qx) < static_cast<double>(px))
+        if (static_cast<double>(d.u[j]) * static_cast<double>(s_qx[j - 1]) < static_cast<double>(px))
           ++a;
         else
           break;
@@ -314,7 +393,8 @@ __device__ int chunk_search(const float (&w)[kPerThread], int c, float t_rel) {
 
 // Choose the chunk of a row whose (rescaled) chunk sums cross u * S.
 // Returns the chunk and writes the target relative to its start.
-__device__ __forceinline__ int pick_chunk_from_stats(const float2* st, int nch, float M, float t, float* t_rel) {
+__device__ __forceinline__ int pick_chunk_from_stats(const float2 (&st)[kMaxChunks], int nch, float M, float t,
+                                                     float* t_rel) {
   float run = 0.f;
   int last_nz = 0;
   for (int c = 0; c < nch; ++c) {
@@ -332,10 +412,10 @@ __device__ __forceinline__ int pick_chunk_from_stats(const float2* st, int nch, 
 
 // Sample from softmax(row r) with uniform u: returns the token.
 template <typename E>
-__device__ int sample_row(const AcceptParams& p, int b, int r, float M, float S, float u) {
-  const float2* st = p.stats + (static_cast<long>(b) * p.rows + r) * p.nch;
+__device__ int sample_row(const AcceptParams& p, const Decision& d, int b, int r, float u) {
+  const float M = d.M[r], S = d.S[r];
   float t_rel;
-  const int c = pick_chunk_from_stats(st, p.nch, M, u * S, &t_rel);
+  const int c = pick_chunk_from_stats(d.st[r], p.nch, M, u * S, &t_rel);
   float x[kPerThread];
   load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
   const float ml = M * kLog2e;
@@ -351,7 +431,7 @@ __device__ __forceinline__ void resid_slice(const AcceptParams& p, int b, const 
   const int a = d.a;
   float x[kPerThread], y[kPerThread];
   load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, a), p.V, c, x);
-  const int qrow = p.in.q_row[b] + a;
+  const int qrow = d.qrow + a;
   load_chunk_slice<E>(row_ptr<E>(p.prev_logits, p.ld, p.rows, b, qrow), p.V, c, y);
   const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
   const float mq_l2 = p.in.q_m[b * (p.N - 1) + a] * kLog2e, inv_sq = 1.f / p.in.q_s[b * (p.N - 1) + a];
@@ -359,41 +439,13 @@ __device__ __forceinline__ void resid_slice(const AcceptParams& p, int b, const 
   for (int k = 0; k < kPerThread; ++k) w[k] = (x[k] == -INFINITY) ? 0.f : resid_weight(x[k], y[k], ma_l2, inv_sa, mq_l2, inv_sq);
 }
 
-// =========================================================== sample kernel
+// ====================================================== finish (one WG)
+// Outputs and next state of sequence b, run by the last workgroup of the
+// sample launch to finish for it: the residual chunk is picked from the
+// slice sums and rescanned here.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p) {
-  const int slice = blockIdx.x, b = blockIdx.y;
-  __shared__ Decision d;
-  decide<E>(p, b, d);
-  if (d.err) return;
-  const int n = d.n, a = d.a;
-  if (a < n) {
-    if (slice >= p.nch) return;
-    float w[kPerThread];
-    resid_slice<E>(p, b, d, slice, w);
-    float local = 0.f;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) local += w[k];
-    const float tot = block_sum(local);
-    if (threadIdx.x == 0) p.resid[static_cast<long>(b) * p.ns + slice] = tot;
-  } else {
-    if (slice >= p.N) return;
-    const int r = n + slice;  // slice 0: bonus row n; slice k: proposal row n + k
-    const int tok = sample_row<E>(p, b, r, d.M[r], d.S[r], d.u[p.N + slice]);
-    if (threadIdx.x == 0) {
-      const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
-      p.samp[b * p.N + slice] = make_int2(tok, __float_as_int(prob_of(l, d.M[r], d.S[r])));
-    }
-  }
-}
-
-// =========================================================== finish kernel
-template <typename E>
-__global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p) {
-  const int b = blockIdx.x;
+__device__ void finish(const AcceptParams& p, int b, const Decision& d) {
   const int N = p.N, nd = N - 1;
-  __shared__ Decision d;
-  decide<E>(p, b, d);
   const int tid = threadIdx.x;
   if (d.err) {
     if (tid == 0) {
@@ -424,11 +476,20 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
   const int n = d.n, a = d.a;
   __shared__ int s_t;
   __shared__ float s_mass;
+  // the other workgroups' results, fetched in parallel
+  __shared__ float s_res[kMaxChunks];
+  __shared__ int2 s_smp[kMaxN];
   if (a < n) {
-    // Residual: pick the chunk from the slice sums, rescan it.
+    if (tid < p.nch) s_res[tid] = get_f32(&p.resid[static_cast<long>(b) * p.nch + tid]);
+  } else if (tid < N) {
+    s_smp[tid] = get_sample(&p.samp[b * N + tid]);
+  }
+  __syncthreads();
+  if (a < n) {
+    // Residual: pick the chunk from the per-chunk sums, rescan it.
     if (tid == 0) {
       float W = 0.f;
-      for (int c = 0; c < p.nch; ++c) W += p.resid[static_cast<long>(b) * p.ns + c];
+      for (int c = 0; c < p.nch; ++c) W += s_res[c];
       s_mass = W;
     }
     __syncthreads();
@@ -443,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
         int c_sel = -1, last_nz = 0;
         float trel = INFINITY;
         for (int c = 0; c < p.nch; ++c) {
-          const float wc = p.resid[static_cast<long>(b) * p.ns + c];
+          const float wc = s_res[c];
           if (wc > 0.f) last_nz = c;
           if (c_sel < 0 && run + wc > t) {
             c_sel = c;
@@ -460,11 +521,11 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
       tok = chunk_search(w, s_c, s_trel);
     } else {
       // No residual mass left (P_a <= Q_{a+1} everywhere): draw from P_a.
-      tok = sample_row<E>(p, b, a, d.M[a], d.S[a], d.u[N]);
+      tok = sample_row<E>(p, d, b, a, d.u[N]);
     }
     if (tid == 0) s_t = tok;
   } else {
-    if (tid == 0) s_t = p.samp[b * N].x;
+    if (tid == 0) s_t = s_smp[0].x;
   }
   __syncthreads();
   if (tid == 0) {
@@ -483,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
       p.out.n_draft[b] = nd;
       p.out.q_row[b] = n + 1;
       for (int k = 1; k <= nd; ++k) {
-        const int2 sp = p.samp[b * N + k];
+        const int2 sp = s_smp[k];
         p.out.drafts[b * nd + k - 1] = sp.x;
         p.out.q_x[b * nd + k - 1] = __int_as_float(sp.y);
         p.out.q_m[b * nd + k - 1] = d.M[n + k];
@@ -511,6 +572,51 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
   }
 }
 
+// =========================================================== sample kernel
+template <typename E>
+__global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p) {
+  const int slice = blockIdx.x, b = blockIdx.y;
+  __shared__ Decision d;
+  decide<E>(p, b, d);
+  const int n = d.n, a = d.a;
+  if (!d.err) {
+    if (a < n) {
+      // residual sums of chunks kStatsChunks * slice ..
+#pragma unroll
+      for (int h = 0; h < kStatsChunks; ++h) {
+        const int c = kStatsChunks * slice + h;
+        if (c < p.nch) {
+          float w[kPerThread];
+          resid_slice<E>(p, b, d, c, w);
+          float local = 0.f;
+#pragma unroll
+          for (int k = 0; k < kPerThread; ++k) local += w[k];
+          const float tot = block_sum(local);
+          if (threadIdx.x == 0) put_f32(&p.resid[static_cast<long>(b) * p.nch + c], tot);
+        }
+      }
+    } else if (slice < p.N) {
+      const int r = n + slice;  // slice 0: bonus row n; slice k: proposal row n + k
+      const int tok = sample_row<E>(p, d, b, r, d.u[p.N + slice]);
+      if (threadIdx.x == 0) {
+        const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
+        put_sample(&p.samp[b * p.N + slice], tok, prob_of(l, d.M[r], d.S[r]));
+      }
+    }
+  }
+  // Arrival: thread 0 made this workgroup's stores; once they are complete
+  // (vmcnt 0) it counts the workgroup in. The one that brings the count to
+  // ns reads everybody's results with device-coherent loads.
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    s_last = __hip_atomic_fetch_add(&p.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.ns - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  finish<E>(p, b, d);
+}
+
 }  // namespace isd
 
 // ================================================================ host API
@@ -521,18 +627,20 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 struct AcceptLayout {
   int nch, ns;
-  size_t stats_off, resid_off, samp_off, total;
+  size_t stats_off, resid_off, samp_off, arrive_off, total;
 };
 
 AcceptLayout accept_layout(int C, int N, int V, int rows) {
   AcceptLayout L;
   L.nch = (V + kChunk - 1) / kChunk;
-  L.ns = L.nch > N ? L.nch : N;
+  const int pairs = (L.nch + kStatsChunks - 1) / kStatsChunks;
+  L.ns = pairs > N ? pairs : N;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   L.stats_off = 0;
   L.resid_off = up(static_cast<size_t>(C) * rows * L.nch * sizeof(float2));
-  L.samp_off = L.resid_off + up(static_cast<size_t>(C) * L.ns * sizeof(float));
-  L.total = L.samp_off + up(static_cast<size_t>(C) * N * sizeof(int2));
+  L.samp_off = L.resid_off + up(static_cast<size_t>(C) * L.nch * sizeof(float));
+  L.arrive_off = L.samp_off + up(static_cast<size_t>(C) * N * sizeof(int2));
+  L.total = L.arrive_off + up(static_cast<size_t>(C) * sizeof(int));
   return L;
 }
 
@@ -540,9 +648,9 @@ bool state_ok(const isd_seq_state& s) { return s.n_draft && s.drafts && s.q_x &&
 
 template <typename E>
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_stats_kernel<E>, dim3(p.nch, 2 * p.N - 1, p.C), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(accept_stats_kernel<E>, dim3((p.nch + kStatsChunks - 1) / kStatsChunks, 2 * p.N - 1, p.C),
+                     dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(accept_sample_kernel<E>, dim3(p.ns, p.C), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(accept_finish_kernel<E>, dim3(p.C), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -551,7 +659,7 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
 extern "C" {
 
 size_t isd_accept_workspace_size(int C, int N, int V, int rows) {
-  if (C < 0 || N < 2 || N > kMaxN || V < 1 || rows < 2 * N - 1) return 0;
+  if (C < 0 || N < 2 || N > kMaxN || V < 1 || V > kMaxChunks * kChunk || rows < 2 * N - 1) return 0;
   return accept_layout(C, N, V, rows).total;
 }
 
@@ -560,6 +668,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   if (a->C < 0 || a->N < 2 || a->V < 1) return ISD_E_INVALID;
   if (a->C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
   if (a->N > kMaxN) return ISD_E_UNSUPPORTED;
+  if (a->V > kMaxChunks * kChunk) return ISD_E_UNSUPPORTED;  // chunk statistics are cached in LDS
   if (a->rows < 2 * a->N - 1) return ISD_E_INVALID;
   if (a->dtype != ISD_BF16 && a->dtype != ISD_F32) return ISD_E_UNSUPPORTED;
   if (a->C == 0) return ISD_OK;
@@ -604,6 +713,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.stats = reinterpret_cast<float2*>(ws + L.stats_off);
   p.resid = reinterpret_cast<float*>(ws + L.resid_off);
   p.samp = reinterpret_cast<int2*>(ws + L.samp_off);
+  p.arrive = reinterpret_cast<int*>(ws + L.arrive_off);
   p.dev_err = a->dev_err;
   const hipError_t e = a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, stream) : launch_accept<float>(p, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;

@@ -173,7 +173,7 @@ typedef struct isd_seq_state {
 typedef struct isd_accept_args {
   int32_t C;     /* sequences, <= 65535 */
   int32_t N;     /* stride, 2..8 */
-  int32_t V;     /* vocabulary size */
+  int32_t V;     /* vocabulary size, <= 524288 */
   int32_t rows;  /* rows per block in logits (>= 2N-1, usually 2N) */
   int32_t dtype; /* logits element type */
   const void* logits;      /* [C][rows][ld] this step's block */
@@ -192,7 +192,8 @@ typedef struct isd_accept_args {
   float* resid_mass;  /* optional [C]: sum max(0, P_a - Q_{a+1}), or -1 */
   float* row_m;       /* optional [C][rows]: max logit of each row read */
   float* row_s;       /* optional [C][rows]: sum exp(l - row_m) */
-  void* ws;
+  void* ws;           /* isd_accept_workspace_size(C, N, V, rows) bytes, 16-byte
+                         aligned, caller-owned, contents on entry ignored */
   size_t ws_bytes;
   int32_t* dev_err;
 } isd_accept_args;

@@ -100,6 +100,10 @@ def test_accept_rejects_bad_arguments_on_host(lib):
     assert lib.isd_accept(ctypes.byref(a), None) == -3  # no workspace
     a.out = st_in
     assert lib.isd_accept(ctypes.byref(a), None) == -1  # out aliases in
+    a.out = st_out
+    a.V, a.ld = 600000, 600000
+    assert lib.isd_accept(ctypes.byref(a), None) == -2  # vocabulary beyond the cached chunk statistics
+    assert lib.isd_accept_workspace_size(64, 4, 600000, 8) == 0
     assert lib.isd_accept_workspace_size(64, 4, 151936, 8) > 0
     assert lib.isd_accept_workspace_size(64, 1, 151936, 8) == 0
 
