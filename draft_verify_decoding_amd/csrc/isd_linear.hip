@@ -31,35 +31,32 @@ constexpr int kXcds = 8;  // XCDs of an MI355X
 
 constexpr int kMaxSplits = 8;  // split-K shares of U = x A^T
 
-// Delta of LoRA rows on the 32x32 output block at (m0, n0): rows of U (fp32
-// [M][r]) against rows of B (bf16 [Nout][r]), r = 16 * R16. Register e of
-// lane (j, hh) is row m0 + 8(e/4) + 4hh + e%4, column n0 + j. Rows and
-// columns past the end contribute zeros.
+// The LoRA delta of one 32x32 output block, U B^T, on bf16 MFMA: each U row
+// (fp32) is split into a bf16 high part (truncation) and the bf16 rounding
+// of the remainder, and the two halves run as two independent MFMA chains
+// added at the end. Register e of lane (j, hh) is block row 8(e/4) + 4hh +
+// e%4, column j. The GEMM epilogue and the stand-alone delta kernel both go
+// through these two functions, so they produce the same bits.
 template <int R16>
-__device__ __forceinline__ f32x16 lora_delta_block(const float* U, const uint16_t* B, int M, int Nout, int m0,
-                                                   int n0, int lane32, int hh) {
-  constexpr int r = 16 * R16;
-  const int arow = m0 + lane32, bcol = n0 + lane32;
-  f32x4 uv[R16][2];
-  u32x4 bv[R16];
+struct UFrag {
+  bf16x8 hi[R16], lo[R16];
+};
+
+// Fragments of the U row this lane feeds to the MFMA (row = block row of
+// lane32; hh selects the 8-entry half of each 16-entry step); null row:
+// zeros.
+template <int R16>
+__device__ __forceinline__ UFrag<R16> u_frag(const float* row, int hh) {
+  UFrag<R16> uf;
 #pragma unroll
   for (int k = 0; k < R16; ++k) {
-    if (arow < M) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(U + static_cast<long>(arow) * r + 16 * k + 8 * hh);
-      uv[k][0] = src[0];
-      uv[k][1] = src[1];
-    } else {
-      uv[k][0] = uv[k][1] = f32x4{};
+    f32x4 v0 = f32x4{}, v1 = f32x4{};
+    if (row) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(row + 16 * k + 8 * hh);
+      v0 = src[0];
+      v1 = src[1];
     }
-    bv[k] = bcol < Nout ? *reinterpret_cast<const u32x4*>(B + static_cast<long>(bcol) * r + 16 * k + 8 * hh)
-                        : u32x4{0, 0, 0, 0};
-  }
-  // two independent MFMA chains (high and low halves), added at the end
-  f32x16 dh = {}, dl = {};
-#pragma unroll
-  for (int k = 0; k < R16; ++k) {
-    const float f[8] = {uv[k][0][0], uv[k][0][1], uv[k][0][2], uv[k][0][3],
-                        uv[k][1][0], uv[k][1][1], uv[k][1][2], uv[k][1][3]};
+    const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     u32x4 hi, lo;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -68,9 +65,29 @@ __device__ __forceinline__ f32x16 lora_delta_block(const float* U, const uint16_
       lo[t] = f32_to_bf16_bits(f[2 * t] - __uint_as_float(ua)) |
               (f32_to_bf16_bits(f[2 * t + 1] - __uint_as_float(ub)) << 16);
     }
+    uf.hi[k] = __builtin_bit_cast(bf16x8, hi);
+    uf.lo[k] = __builtin_bit_cast(bf16x8, lo);
+  }
+  return uf;
+}
+
+// U B^T for columns n0.. of B (bf16 [Nout][r]); columns past Nout give 0.
+template <int R16>
+__device__ __forceinline__ f32x16 lora_delta(const UFrag<R16>& uf, const uint16_t* B, int Nout, int n0, int lane32,
+                                             int hh) {
+  constexpr int r = 16 * R16;
+  const int bcol = n0 + lane32;
+  u32x4 bv[R16];
+#pragma unroll
+  for (int k = 0; k < R16; ++k)
+    bv[k] = bcol < Nout ? *reinterpret_cast<const u32x4*>(B + static_cast<long>(bcol) * r + 16 * k + 8 * hh)
+                        : u32x4{0, 0, 0, 0};
+  f32x16 dh = {}, dl = {};
+#pragma unroll
+  for (int k = 0; k < R16; ++k) {
     const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[k]);
-    dh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi), bb, dh, 0, 0, 0);
-    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo), bb, dl, 0, 0, 0);
+    dh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf.hi[k], bb, dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf.lo[k], bb, dl, 0, 0, 0);
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) dh[e] += dl[e];
@@ -82,7 +99,7 @@ struct GemmParams {
   const uint16_t* w;    // [Nout][K]
   float* y;             // [splits][M][Nout]
   // gated epilogue (R16 > 0): MASK rows get y = acc + scale * U B^T
-  const float* u;       // [M][r] fp32
+  const float* u;       // [M][r] fp32 U = x A^T
   const uint16_t* b;    // [Nout][r]
   const uint8_t* mask;  // [M]
   float scale;
@@ -236,23 +253,49 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   }
   wait_vm_lgkm0<0>();
 
+  // Gated: the workgroup copies the U rows of its BM rows into LDS, reusing
+  // the stages (rows padded by 4 floats so the fragment reads spread over the
+  // banks); each wave then splits its rows once for all of its column blocks.
+  constexpr int kUStride = 16 * R16 + 4;
+  constexpr int kURowsPerStage = R16 > 0 ? (STAGE * 2) / (kUStride * 4) : 1;
+  static_assert(R16 == 0 || (BM + kURowsPerStage - 1) / kURowsPerStage <= STAGES, "U cache fits the stages");
+  auto urow = [&](int row) -> float* {
+    return reinterpret_cast<float*>(stage_ptr(row / kURowsPerStage)) + (row % kURowsPerStage) * kUStride;
+  };
+  if constexpr (R16 > 0) {
+    constexpr int r4 = 4 * R16;  // float4 per U row
+    stage_barrier();             // every wave is done with the stages
+    for (int e = tid; e < BM * r4; e += 256) {
+      const int row = e / r4, q = e % r4;
+      const float* src = p.u + static_cast<long>(min(m_blk + row, p.M - 1)) * 16 * R16 + 4 * q;
+      *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = *reinterpret_cast<const f32x4*>(src);
+    }
+    wait_vm_lgkm0<0>();
+    stage_barrier();
+  }
+
   // Epilogue: register e of lane (j, hh) is row 8(e/4) + 4hh + e%4 of the
   // 32x32 block, column j. Gated: a MASK row takes acc + scale * delta, a
   // clean row takes acc itself.
   float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int m0 = m_blk + wm + 32 * i;
+    int live = 0;
+    UFrag<(R16 > 0 ? R16 : 1)> uf;
+    if constexpr (R16 > 0) {
+      const int mine = m0 + lane32 < p.M ? p.mask[m0 + lane32] != 0 : 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) live |= __shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) << e;
+      if (__any(live)) uf = u_frag<R16>(urow(wm + 32 * i + lane32), hh);  // rows past M: never stored
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int m0 = m_blk + wm + 32 * i, n0 = n_blk + wn + 32 * j;
+      const int n0 = n_blk + wn + 32 * j;
       const int col = n0 + lane32;
       f32x16 dl = {};
-      int live = 0;
       if constexpr (R16 > 0) {
-        const int mine = m0 + lane32 < p.M ? p.mask[m0 + lane32] != 0 : 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) live |= __shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) << e;
-        if (__any(live)) dl = lora_delta_block<R16>(p.u, p.b, p.M, p.Nout, m0, n0, lane32, hh);
+        if (__any(live)) dl = lora_delta<R16>(uf, p.b, p.Nout, n0, lane32, hh);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -261,6 +304,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
           y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[i][j][e]) : acc[i][j][e];
       }
     }
+  }
 }
 
 // y[m] += scale * (U B^T)[m] on MASK rows only, one wave per 32x32 tile of
@@ -296,7 +340,8 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
     const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
     yv[e] = ((live >> e) & 1) ? p.y[static_cast<long>(row) * p.Nout + bcol] : 0.f;
   }
-  const f32x16 dl = lora_delta_block<R16>(p.u, p.b, p.M, p.Nout, m0, n0, lane32, hh);
+  const UFrag<R16> uf = u_frag<R16>(m0 + lane32 < p.M ? p.u + static_cast<long>(m0 + lane32) * 16 * R16 : nullptr, hh);
+  const f32x16 dl = lora_delta<R16>(uf, p.b, p.Nout, n0, lane32, hh);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if ((live >> e) & 1) {
@@ -376,23 +421,27 @@ int u_splits(int K) {
 
 size_t part_bytes(int M, int r) { return (static_cast<size_t>(M) * r * sizeof(float) * kMaxSplits + 255) & ~static_cast<size_t>(255); }
 
-// U = x A^T into the workspace: split-K partials, then their sum.
-hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
-  float* part = static_cast<float*>(ws);
-  float* U = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(M, r));
+// Split-K partials of U = x A^T at the start of the workspace.
+hipError_t launch_lora_u_partials(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
   GemmParams g{};
   g.x = static_cast<const uint16_t*>(x);
   g.w = static_cast<const uint16_t*>(A);
-  g.y = part;
+  g.y = static_cast<float*>(ws);
   g.M = M;
   g.K = K;
   g.Nout = r;
   g.splits = u_splits(K);
-  hipError_t e = launch_gemm_r<0>(g, stream);
+  return launch_gemm_r<0>(g, stream);
+}
+
+// U = x A^T into the workspace: split-K partials, then their sum.
+hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
+  hipError_t e = launch_lora_u_partials(x, A, M, K, r, ws, stream);
   if (e != hipSuccess) return e;
+  float* U = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(M, r));
   const long n = static_cast<long>(M) * r;
-  hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, part,
-                     U, n, g.splits);
+  hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const float*>(ws), U, n, u_splits(K));
   return hipGetLastError();
 }
 
