@@ -480,8 +480,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 // Log-sum-exp merge of the pieces of one (sequence, KV head, query block)
-// held by several slices, in slice order. Thread t owns query column t/8
-// and D/8 consecutive dims, read and written as float4.
+// held by several slices, in slice order (an online rescale, so the pieces
+// are read once). Thread t owns query column t/8 and D/8 consecutive dims,
+// read and written as float4; the (max, sum) and vectors of up to eight
+// pieces are loaded together before any is combined.
 template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   const int MB = p.MB;
@@ -498,6 +500,8 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   const int wa = slice_of(tb0), wb = slice_of(tb1 - 1);
   if (wa == wb) return;  // finalised by its slice
   constexpr int kDimsPerThread = D * 32 / 256;
+  constexpr int kV = kDimsPerThread / 4;
+  constexpr int kBatch = 8;
   const int col = qb * 32 + threadIdx.x / (256 / 32);
   const int d0 = (threadIdx.x % (256 / 32)) * kDimsPerThread;
   if (col >= p.M) return;
@@ -508,32 +512,44 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   };
   // a slice whose range is empty (more slices than tiles) holds no piece
   auto empty = [&](int w2) { return (w2 * T / G) == ((w2 + 1) * T / G); };
-  float mstar = -1e30f;
-  for (int w2 = wa; w2 <= wb; ++w2)
-    if (!empty(w2)) mstar = fmaxf(mstar, p.part_ml[piece(w2) * 2]);
-  f32x4 acc[kDimsPerThread / 4];
+  float m_run = -1e30f, l_run = 0.f;  // finite floor: exp2(m_run - m_new) stays defined
+  f32x4 acc[kV];
 #pragma unroll
-  for (int k = 0; k < kDimsPerThread / 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  for (int w2 = wa; w2 <= wb; ++w2) {
-    if (empty(w2)) continue;
-    const size_t idx = piece(w2);
-    const float wt = fast_exp2(p.part_ml[idx * 2] - mstar);
-    lsum = fmaf(wt, p.part_ml[idx * 2 + 1], lsum);
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
+  for (int k = 0; k < kV; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w0 = wa; w0 <= wb; w0 += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    f32x4 ov[kBatch][kV];
+    bool has[kBatch];
 #pragma unroll
-    for (int k = 0; k < kDimsPerThread / 4; ++k) {
-      const f32x4 v = src[k];
+    for (int j = 0; j < kBatch; ++j) {
+      const int w2 = w0 + j;
+      has[j] = w2 <= wb && !empty(w2);
+      const size_t idx = piece(has[j] ? w2 : wa);  // slice wa holds a piece
+      mv[j] = p.part_ml[idx * 2];
+      lv[j] = p.part_ml[idx * 2 + 1];
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(wt, v[e], acc[k][e]);
+      for (int k = 0; k < kV; ++k) ov[j][k] = src[k];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (!has[j]) continue;
+      const float m_new = fmaxf(m_run, mv[j]);
+      const float a = fast_exp2(m_run - m_new), c = fast_exp2(mv[j] - m_new);
+      l_run = fmaf(l_run, a, lv[j] * c);
+#pragma unroll
+      for (int k = 0; k < kV; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(acc[k][e], a, ov[j][k][e] * c);
+      m_run = m_new;
     }
   }
   const int hl = col / p.rows, i = col % p.rows;
   const int h = g * p.group + hl;
   f32x4* dst = reinterpret_cast<f32x4*>(p.out + ((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d0);
-  const float inv = 1.f / lsum;
+  const float inv = 1.f / l_run;
 #pragma unroll
-  for (int k = 0; k < kDimsPerThread / 4; ++k) {
+  for (int k = 0; k < kV; ++k) {
     f32x4 v = acc[k];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * inv;
