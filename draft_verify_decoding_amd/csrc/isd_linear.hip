@@ -171,20 +171,22 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   // Slabs go from global memory straight into LDS (16-byte direct loads, no
   // register staging). A stage holds the slab's BM rows of x, then its BN rows
   // of W, 128 bytes per row with the 16-byte chunks XOR-swizzled: chunk c of
-  // row r sits at slot c ^ (r % 8), so both the loads (lane i of a load
-  // fills slot i % 8 of row i / 8 of an 8-row group) and the MFMA operand
-  // reads (eight rows at one chunk) touch every bank once. Rows past the end
+  // row r sits at slot c ^ (r % 8) ^ ((r / 8) % 2). The loads (lane i of a
+  // load fills slot i % 8 of row i / 8 of an 8-row group) and the MFMA
+  // operand reads (sixteen rows at one chunk, which land in both halves of
+  // a 64-bank LDS line pair) then touch every bank once. Rows past the end
   // read the last valid row: output row i depends only on A row i and column
   // j only on B row j, and such rows and columns are never written.
-  const int g_row = lane >> 3, g_chunk = (lane & 7) ^ (lane >> 3);
+  const int g_row = lane >> 3;
+  auto g_chunk = [&](int group) { return (lane & 7) ^ g_row ^ (group & 1); };  // group = 8-row group index
   const uint16_t* a_src[A_LOADS];
   const uint16_t* b_src[B_LOADS];
 #pragma unroll
   for (int q = 0; q < A_LOADS; ++q)
-    a_src[q] = p.x + static_cast<long>(min(m_blk + 8 * (wave + 4 * q) + g_row, p.M - 1)) * p.K + 8 * g_chunk;
+    a_src[q] = p.x + static_cast<long>(min(m_blk + 8 * (wave + 4 * q) + g_row, p.M - 1)) * p.K + 8 * g_chunk(wave + 4 * q);
 #pragma unroll
   for (int q = 0; q < B_LOADS; ++q)
-    b_src[q] = p.w + static_cast<long>(min(n_blk + 8 * (wave + 4 * q) + g_row, p.Nout - 1)) * p.K + 8 * g_chunk;
+    b_src[q] = p.w + static_cast<long>(min(n_blk + 8 * (wave + 4 * q) + g_row, p.Nout - 1)) * p.K + 8 * g_chunk(wave + 4 * q);
   auto load_slab = [&](int k0, int stage) {
     uint16_t* base = stage_ptr(stage);
 #pragma unroll
@@ -201,25 +203,40 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  const int sw = lane32 & 7;  // row % 8 of every operand row this lane reads
+  const int sw = (lane32 & 7) ^ ((lane32 >> 3) & 1);  // swizzle of every operand row this lane reads
+  // The operand fragments of step s+1 are read while step s multiplies.
   auto compute = [&](int stage) {
     const uint16_t* sA = stage_ptr(stage);
     const uint16_t* sB = sA + BM * kBK;
+    constexpr int kSteps = kBK / 16;
+    bf16x8 a[kSteps][TM], b[kSteps][TN];
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
       const int slot = ((2 * s + hh) ^ sw) * 8;
-      bf16x8 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sA[(wm + 32 * i + lane32) * kBK + slot]));
+        a[s][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sA[(wm + 32 * i + lane32) * kBK + slot]));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sB[(wn + 32 * j + lane32) * kBK + slot]));
+        b[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sB[(wn + 32 * j + lane32) * kBK + slot]));
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+    // Software pipeline: the reads of step s+1 are issued right after the
+    // MFMAs of step s (the scheduler would otherwise wait on LDS before
+    // every step).
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < kSteps; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
   };
 
   // STAGES-1 slabs in flight ahead of the one being multiplied. Slabs past
