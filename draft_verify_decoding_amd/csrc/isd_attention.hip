@@ -565,12 +565,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(void* k_pages, void* v_pa
                                                        int rows, int32_t* dev_err) {
   constexpr int KP = Elem<E>::kPerVec;
   const int per_row = Hkv * (D / KP);
-  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long>(C) * rows * per_row) return;
-  const int c = static_cast<int>(idx % (D / KP));
-  const int g = static_cast<int>((idx / (D / KP)) % Hkv);
-  const int r = static_cast<int>((idx / per_row) % rows);
-  const int b = static_cast<int>(idx / (static_cast<long>(per_row) * rows));
+  // grid (chunks of one sequence's rows, sequences): b is uniform, so its
+  // position and row count come in through scalar loads
+  const int b = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * per_row) return;
+  const int c = idx % (D / KP);
+  const int g = (idx / (D / KP)) % Hkv;
+  const int r = idx / per_row;
+  // the row's K/V values do not depend on where they go: fetch them first
+  const size_t src = ((static_cast<size_t>(b) * rows + r) * Hkv + g) * D + c * KP;
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src);
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src);
   const int nr = nrows ? nrows[b] : rows;
   if (r >= nr) return;
   const int pos = pos0[b] + r;
@@ -588,9 +594,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(void* k_pages, void* v_pa
     set_dev_err(dev_err, ISD_DEV_PAGE_OOB);
     return;
   }
-  const size_t src = ((static_cast<size_t>(b) * rows + r) * Hkv + g) * D + c * KP;
-  const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src);
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src);
   E* kpage = static_cast<E*>(k_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
   E* vpage = static_cast<E*>(v_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
   *reinterpret_cast<u32x4*>(kpage + (c * 16 + slot) * KP) = kv;
@@ -732,14 +735,15 @@ int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v, const int
   if (rc) return rc;
   if (C < 0 || rows < 0) return ISD_E_INVALID;
   if (C == 0 || rows == 0) return ISD_OK;
+  if (C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
   if (!k || !v || !pos0) return ISD_E_INVALID;
   if (!aligned16(k) || !aligned16(v)) return ISD_E_INVALID;
   rc = isd_check_device_internal();
   if (rc) return rc;
   const int D = kv->head_dim;
   const int KP = kv->dtype == ISD_BF16 ? 8 : 4;
-  const long total = static_cast<long>(C) * rows * kv->num_kv_heads * (D / KP);
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  const long per_seq = static_cast<long>(rows) * kv->num_kv_heads * (D / KP);
+  const dim3 grid(static_cast<unsigned>((per_seq + 255) / 256), static_cast<unsigned>(C));
 #define ISD_KVW(E, DD)                                                                                          \
   hipLaunchKernelGGL((kv_write_kernel<E, DD>), grid, dim3(256), 0, stream, kv->k_pages, kv->v_pages,            \
                      kv->block_table, kv->table_stride, kv->num_pages, kv->num_kv_heads, static_cast<const E*>(k), \

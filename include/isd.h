@@ -100,7 +100,8 @@ typedef struct isd_kv_cache {
  * position pos0[b] + r. k and v are [C][rows][Hkv][D] in kv->dtype.
  * nrows may be NULL (every sequence writes `rows` rows). Positions whose
  * page column is >= table_stride or whose page id is outside the pool are
- * skipped and flagged (ISD_DEV_CAPACITY / ISD_DEV_PAGE_OOB). */
+ * skipped and flagged (ISD_DEV_CAPACITY / ISD_DEV_PAGE_OOB). C <= 65535
+ * (else ISD_E_UNSUPPORTED); k and v must be 16-byte aligned. */
 int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
                  const int32_t* pos0, const int32_t* nrows, int C, int rows,
                  int32_t* dev_err, hipStream_t stream);

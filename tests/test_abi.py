@@ -80,6 +80,14 @@ def test_attention_rejects_bad_arguments_on_host(lib):
                              None) == -3
 
 
+def test_kv_write_rejects_bad_arguments_on_host(lib):
+    kv = dvd.IsdKvCache(16, 16, 16, 4, 10, 16, 1, 128, dvd.ISD_BF16)
+    assert lib.isd_kv_write(ctypes.byref(kv), 16, 16, 16, None, 0, 8, None, None) == 0  # nothing to write
+    assert lib.isd_kv_write(ctypes.byref(kv), 16, 16, 16, None, 70000, 8, None, None) == -2  # C beyond the grid
+    assert lib.isd_kv_write(ctypes.byref(kv), 18, 16, 16, None, 2, 8, None, None) == -1  # misaligned k
+    assert lib.isd_kv_write(ctypes.byref(kv), 16, 16, None, None, 2, 8, None, None) == -1  # no positions
+
+
 def test_accept_rejects_bad_arguments_on_host(lib):
     assert lib.isd_accept(None, None) == -1
     a = dvd.IsdAcceptArgs()
