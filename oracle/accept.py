@@ -67,8 +67,17 @@ def inv_cdf(w, u):
     return v, float(margin)
 
 
-def accept_step(logits, prev_logits, n_draft, drafts, q_row, u, N):
+def accept_step(logits, prev_logits, n_draft, drafts, q_row, u, N, proposal="sample"):
     """One accept step for a batch of C sequences.
+
+    proposal "sample" (the default): drafts are drawn from the MASK rows'
+    softmax q and verified with min(1, p/q). proposal "argmax": the pages'
+    serving stack proposes argmax q instead (I-DLM, fr.news.hada.io,
+    "Documentation et ressources > Serving (SGLang)": argmax proposal); q is
+    then a point mass at the draft, so the same rule reads accept iff
+    u < p(x), and the residual max(0, p - q) is p with the draft removed.
+    (The pages do not spell out that rule; it is the standard rejection step
+    with a point-mass proposal.) Ties of the argmax go to the smallest id.
 
     logits      float64 [C, R, V]   this step's block logits (R >= 2N-1 used)
     prev_logits float64 [C, R', V]  the previous step's block (q rows of the
@@ -115,7 +124,12 @@ def accept_step(logits, prev_logits, n_draft, drafts, q_row, u, N):
         P = [softmax(logits[b, j]) for j in range(n + 1)]
 
         def q_dist(j):
-            return softmax(prev_logits[b, int(q_row[b]) + j - 1])
+            row = prev_logits[b, int(q_row[b]) + j - 1]
+            if proposal == "argmax":
+                q = np.zeros(V)
+                q[int(np.argmax(row))] = 1.0
+                return q
+            return softmax(row)
 
         a = 0
         for j in range(1, n + 1):
@@ -144,10 +158,16 @@ def accept_step(logits, prev_logits, n_draft, drafts, q_row, u, N):
             t, margin = inv_cdf(P[n], u[b, N])
             out["final_margin"][b] = margin
             for k in range(1, N):
-                Qk = softmax(logits[b, n + k])
-                xk, mk = inv_cdf(Qk, u[b, N + k])
+                if proposal == "argmax":
+                    # exact comparisons of the same values on both sides:
+                    # no boundary to be near
+                    xk, qx, mk = int(np.argmax(logits[b, n + k])), 1.0, np.inf
+                else:
+                    Qk = softmax(logits[b, n + k])
+                    xk, mk = inv_cdf(Qk, u[b, N + k])
+                    qx = Qk[xk]
                 out["drafts_next"][b, k - 1] = xk
-                out["q_x_next"][b, k - 1] = Qk[xk]
+                out["q_x_next"][b, k - 1] = qx
                 out["propose_margin"][b, k - 1] = mk
             out["n_draft_next"][b] = nd
             out["q_row_next"][b] = n + 1

@@ -258,3 +258,87 @@ def test_flagged_marks_near_boundary_draws():
     assert accept.flagged(out).tolist() == [True, True]
     out["propose_margin"][1, 1] = 0.2
     assert accept.flagged(out).tolist() == [True, False]
+
+
+# ------------------------------------------------ argmax proposals (reading)
+
+def argmax_step(P_rows, Q_rows, u, N):
+    """FULL step with argmax proposals: the drafts are argmax of the q rows."""
+    drafts = np.argmax(Q_rows, axis=-1)
+    C = u.shape[0]
+    V = P_rows.shape[-1]
+    R = 2 * N
+    cur = np.zeros((C, R, V))
+    cur[:, :N] = logits_of(P_rows)
+    prev = np.zeros((C, R, V))
+    prev[:, 1:N] = logits_of(Q_rows)
+    n, d, qr = full_state(C, N, drafts)
+    return accept.accept_step(cur, prev, n, d, qr, u, N, proposal="argmax"), drafts
+
+
+def test_argmax_first_emitted_token_exact_enumeration():
+    """A point-mass proposal still leaves the first emitted token distributed
+    as P_0: enumerate both uniforms over a midpoint grid (V = 4, N = 2)."""
+    P = np.array([0.1, 0.4, 0.3, 0.2])
+    Q = np.array([0.1, 0.2, 0.6, 0.1])  # argmax 2
+    N, G = 2, 64
+    grid = (np.arange(G) + 0.5) / G
+    C = G * G
+    uu = np.zeros((C, 2 * N))
+    uu[:, 1] = np.repeat(grid, G)
+    uu[:, N] = np.tile(grid, G)
+    out, drafts = argmax_step(np.broadcast_to(P, (C, N, 4)), np.broadcast_to(Q, (C, 1, 4)), uu, N)
+    assert (drafts == 2).all()
+    prob = np.bincount(out["emit"][:, 0], minlength=4) / C
+    assert np.allclose(prob, P, atol=2.0 / G)
+    # acceptance is P(x) exactly (to the grid), and a rejection never emits x
+    assert abs(out["accepted"].mean() - P[2]) <= 1.0 / G
+    assert (out["emit"][out["accepted"] == 0, 0] != 2).all()
+    assert np.allclose(out["q_x"][:, 0], 1.0)
+
+
+def test_argmax_proposals_and_residual_mass():
+    rng = np.random.default_rng(11)
+    V, N, C = 7, 3, 4000
+    P = rng.dirichlet(np.ones(V), size=N)
+    Q = rng.dirichlet(np.ones(V), size=N - 1)
+    u = rng.random((C, 2 * N))
+    out, drafts = argmax_step(np.broadcast_to(P, (C, N, V)), np.broadcast_to(Q, (C, N - 1, V)), u, N)
+    # chi-square of the first emitted token against P_0
+    counts = np.bincount(out["emit"][:, 0], minlength=V)
+    chi2, pval = stats.chisquare(counts, P[0] * C)
+    assert pval > 1e-4, (chi2, pval)
+    # the residual after rejecting x_1 is P_0 without x_1: its mass is 1 - P_0(x_1)
+    rej = out["accepted"] == 0
+    x1 = int(np.argmax(Q[0]))
+    assert np.allclose(out["resid_mass"][rej], 1.0 - P[0][x1])
+    # new drafts, when all pass, are the argmax of the proposal rows
+    full = out["accepted"] == N - 1
+    assert full.any()
+    assert np.isinf(out["propose_margin"][full]).all() and np.allclose(out["q_x_next"][full], 1.0)
+
+
+def test_argmax_loop_reproduces_closed_form():
+    """Decoding loop with argmax proposals where every draft passes with
+    probability p = P(argmax Q): tokens per forward follows the pages'
+    closed form at that p."""
+    N, p = 4, 0.7
+    P = np.array([p, 1.0 - p])
+    Q = np.array([0.8, 0.2])  # argmax 0, accepted with probability P[0] = p
+    lp, lq = logits_of(P), logits_of(Q)
+    C, steps, R = 48, 160, 2 * N
+    n = np.zeros(C, int)
+    drafts = np.full((C, N - 1), -1)
+    q_row = np.zeros(C, int)
+    prev = None
+    tokens = 0
+    for step in range(steps):
+        cur = np.empty((C, R, 2))
+        r = np.arange(R)[None, :, None]
+        cur[:] = np.where(r <= n[:, None, None], lp, lq)
+        u = philox.step_uniforms(77, step, C, N)
+        out = accept.accept_step(cur, prev, n, drafts, q_row, u, N, proposal="argmax")
+        tokens += out["n_emit"].sum()
+        n, drafts, q_row, prev = out["n_draft_next"], out["drafts_next"], out["q_row_next"], cur
+    tpf = tokens / (C * steps)
+    assert abs(tpf - chain.tpf_closed_form(N, p)) < 0.08, tpf
