@@ -38,7 +38,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 PROBE_EVERY = 8  # timed steps between the ones bracketed with HIP events
 
 CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, lora_rank=32,
-           ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3)
+           ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3, proposal="sample")
 
 
 def log(*a):
@@ -209,7 +209,7 @@ def dry_run(cfg, steps_total, ctx0, dev):
         lg = teacher.block(t, ctx.long(), ctx0_t, s_in.n_draft.long(), R).contiguous()
         ctxs.append(ctx.cpu().numpy().copy())
         nds.append(s_in.n_draft.cpu().numpy().copy())
-        out = dvd.isd_accept(lg, prev, s_in, s_out, N, cfg["seed"], t, ws=ws, ctx=ctx)
+        out = dvd.isd_accept(lg, prev, s_in, s_out, N, cfg["seed"], t, ws=ws, ctx=ctx, proposal=cfg["proposal"])
         accs.append(out.accepted.cpu().numpy().copy())
         logits.append(lg)
         prev = lg
@@ -305,6 +305,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slices", type=int, default=0, help="attention workgroups per KV-head group (0 = automatic)")
+    ap.add_argument("--proposal", choices=("sample", "argmax"), default="sample",
+                    help="draft proposals: sampled from q (default) or argmax q")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -330,7 +332,7 @@ def main():
 
     import draft_verify_decoding_amd as dvd
 
-    cfg = dict(CFG)
+    cfg = dict(CFG, proposal=args.proposal)
     dev = "cuda"
     torch.cuda.set_device(0)
     dvd.lib()
@@ -401,7 +403,7 @@ def main():
         if timed_idx is not None:
             acc_ev[timed_idx][0].record()
         dvd.isd_accept(logits[t], logits[t - 1] if t else None, s_in, s_out, N, cfg["seed"], t, out=acc_out,
-                       ws=acc_ws, ctx=ctx, dev_err=err)
+                       ws=acc_ws, ctx=ctx, dev_err=err, proposal=cfg["proposal"])
         if timed_idx is not None:
             acc_ev[timed_idx][1].record()
 
@@ -457,6 +459,7 @@ def main():
                         "acceptance ~0.9, gated-LoRA rank-32 Q/K/V/O projections; MLP and LM head not included",
             "C": C, "N": N, "layers": L, "Hq": Hq, "Hkv": cfg["Hkv"], "head_dim": D, "vocab": V,
             "global_batch": C, "seq_len": int(np.mean(ctxs[W])), "parallelism": "none (1 GPU)",
+            "proposal": cfg["proposal"],
         },
         "roofline": {
             "kernel": "isd_attention (main + LSE merge launches of one call)",

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libisd.so")
 
 ISD_BF16 = 1
 ISD_F32 = 2
+PROPOSE = {"sample": 0, "argmax": 1}
 PAGE_SIZE = 16
 
 DEV_PAGE_OOB = 1
@@ -67,6 +68,7 @@ class IsdAcceptArgs(ctypes.Structure):
         ("row_m", ctypes.c_void_p), ("row_s", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("dev_err", ctypes.c_void_p),
+        ("proposal", ctypes.c_int32),
     ]
 
 
@@ -238,10 +240,11 @@ class AcceptOutputs:
 
 
 def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
-               diag=False, dev_err=None, ctx=None, stream=None):
+               diag=False, dev_err=None, ctx=None, stream=None, proposal="sample"):
     """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
     AcceptOutputs (device tensors) and writes state_out. If ctx (int32 [C])
-    is given, the kernel adds kv_commit to it."""
+    is given, the kernel adds kv_commit to it. proposal: "sample" or
+    "argmax" (drafts = argmax of the MASK rows)."""
     C, rows, ld = logits.shape
     V = ld if V is None else V
     if out is None:
@@ -267,6 +270,7 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     args.ws = ws.data_ptr()
     args.ws_bytes = ws.numel() * ws.element_size()
     args.dev_err = None if dev_err is None else dev_err.data_ptr()
+    args.proposal = PROPOSE[proposal]
     _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
     return out
 

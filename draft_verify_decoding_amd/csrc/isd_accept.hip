@@ -49,6 +49,7 @@ struct AcceptParams {
   int2* samp;       // [C][N] (token, bits of q(x)) from the sample kernel
   int* arrive;      // [C] workgroups of the sample launch done, per sequence
   int32_t* dev_err;
+  int argmax;       // proposals are argmax q (a point mass at the draft)
 };
 
 // ------------------------------------------- values handed between workgroups
@@ -267,6 +268,7 @@ struct Decision {
   float S[2 * kMaxN];                // row sum exp(l - M)
   float u[2 * kMaxN];                // uniforms by slot
   float px[kMaxN];                   // P_{j-1}(x_j) of tested drafts
+  int draft[kMaxN];                  // pending draft ids
   float2 st[2 * kMaxN][kMaxChunks];  // chunk (max, sum) of the rows read
 };
 
@@ -287,6 +289,7 @@ __device__ void decide(const AcceptParams& p, int b, Decision& d) {
   if (tid < nd) {
     s_draft[tid] = p.in.drafts[b * nd + tid];
     s_qx[tid] = p.in.q_x[b * nd + tid];
+    d.draft[tid] = s_draft[tid];
   }
   for (int i = tid; i < R * p.nch; i += kThreads)
     d.st[i / p.nch][i % p.nch] = p.stats[(static_cast<long>(b) * p.rows + i / p.nch) * p.nch + i % p.nch];
@@ -299,7 +302,7 @@ __device__ void decide(const AcceptParams& p, int b, Decision& d) {
   if (tid == 0) {
     int err = 0;
     if (n_raw < 0 || n_raw > nd) err |= ISD_DEV_STATE;
-    if (n > 0 && (!p.prev_logits || d.qrow < 0 || d.qrow + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
+    if (n > 0 && ((!p.argmax && !p.prev_logits) || d.qrow < 0 || d.qrow + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
     for (int j = 0; j < n; ++j)
       if (s_draft[j] < 0 || s_draft[j] >= p.V) err |= ISD_DEV_TOKEN_OOB;
     d.n = n;
@@ -424,13 +427,50 @@ __device__ int sample_row(const AcceptParams& p, const Decision& d, int b, int r
   return chunk_search(x, c, t_rel);
 }
 
-// Residual weights of this thread's slice of chunk c.
+// argmax of row r, ties to the smallest id: the first chunk whose maximum is
+// the row maximum holds it; its entries are compared exactly with that value.
+template <typename E>
+__device__ int argmax_row(const AcceptParams& p, const Decision& d, int b, int r) {
+  __shared__ int s_tok;
+  const float M = d.M[r];
+  int c = 0;
+  while (c + 1 < p.nch && d.st[r][c].x != M) ++c;
+  if (threadIdx.x == 0) s_tok = 0x7fffffff;
+  __syncthreads();
+  float x[kPerThread];
+  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  int hit = 0x7fffffff;
+#pragma unroll
+  for (int k = kPerThread - 1; k >= 0; --k)
+    if (x[k] == M) hit = v0 + k;
+  if (hit != 0x7fffffff) atomicMin(&s_tok, hit);
+  __syncthreads();
+  const int tok = s_tok;
+  __syncthreads();
+  return tok;
+}
+
+// Residual weights of this thread's slice of chunk c. With argmax proposals
+// Q_{a+1} is a point mass at the rejected draft: the residual is P_a with
+// that token removed, and the previous block is not read.
 template <typename E>
 __device__ __forceinline__ void resid_slice(const AcceptParams& p, int b, const Decision& d, int c,
                                             float (&w)[kPerThread]) {
   const int a = d.a;
   float x[kPerThread], y[kPerThread];
   load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, a), p.V, c, x);
+  if (p.argmax) {
+    const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
+    const int x_rej = d.draft[a], v0 = c * kChunk + threadIdx.x * kPerThread;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+#pragma clang fp contract(off)
+      const float pa = weight_of(x[k], ma_l2) * inv_sa;
+      w[k] = (x[k] == -INFINITY || v0 + k == x_rej) ? 0.f : pa;
+    }
+    return;
+  }
   const int qrow = d.qrow + a;
   load_chunk_slice<E>(row_ptr<E>(p.prev_logits, p.ld, p.rows, b, qrow), p.V, c, y);
   const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
@@ -597,10 +637,15 @@ __global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p)
       }
     } else if (slice < p.N) {
       const int r = n + slice;  // slice 0: bonus row n; slice k: proposal row n + k
-      const int tok = sample_row<E>(p, d, b, r, d.u[p.N + slice]);
-      if (threadIdx.x == 0) {
-        const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
-        put_sample(&p.samp[b * p.N + slice], tok, prob_of(l, d.M[r], d.S[r]));
+      if (p.argmax && slice > 0) {
+        const int tok = argmax_row<E>(p, d, b, r);
+        if (threadIdx.x == 0) put_sample(&p.samp[b * p.N + slice], tok, 1.f);
+      } else {
+        const int tok = sample_row<E>(p, d, b, r, d.u[p.N + slice]);
+        if (threadIdx.x == 0) {
+          const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
+          put_sample(&p.samp[b * p.N + slice], tok, prob_of(l, d.M[r], d.S[r]));
+        }
       }
     }
   }
@@ -671,6 +716,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   if (a->V > kMaxChunks * kChunk) return ISD_E_UNSUPPORTED;  // chunk statistics are cached in LDS
   if (a->rows < 2 * a->N - 1) return ISD_E_INVALID;
   if (a->dtype != ISD_BF16 && a->dtype != ISD_F32) return ISD_E_UNSUPPORTED;
+  if (a->proposal != ISD_PROPOSE_SAMPLE && a->proposal != ISD_PROPOSE_ARGMAX) return ISD_E_INVALID;
   if (a->C == 0) return ISD_OK;
   if (!a->logits || !state_ok(a->in) || !state_ok(a->out)) return ISD_E_INVALID;
   if (!a->accepted || !a->n_emit || !a->emit || !a->kv_commit) return ISD_E_INVALID;
@@ -714,6 +760,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.resid = reinterpret_cast<float*>(ws + L.resid_off);
   p.samp = reinterpret_cast<int2*>(ws + L.samp_off);
   p.arrive = reinterpret_cast<int*>(ws + L.arrive_off);
+  p.argmax = a->proposal == ISD_PROPOSE_ARGMAX;
   p.dev_err = a->dev_err;
   const hipError_t e = a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, stream) : launch_accept<float>(p, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;

@@ -25,7 +25,7 @@ const char* isd_strerror(int code) {
   }
 }
 
-int isd_version(void) { return 100; }
+int isd_version(void) { return 101; }
 
 // Per-device facts, looked up once: 0 unknown, else 1 + CU count for a
 // gfx950 device, or -1 for any other device.

@@ -63,6 +63,10 @@ extern "C" {
 #define ISD_BF16 1
 #define ISD_F32 2
 
+/* Proposal rule of isd_accept (see there). */
+#define ISD_PROPOSE_SAMPLE 0 /* drafts drawn from q, verified with min(1, p/q) */
+#define ISD_PROPOSE_ARGMAX 1 /* drafts = argmax q (a point mass)            */
+
 #define ISD_PAGE_SIZE 16 /* tokens per KV page */
 
 const char* isd_strerror(int code);
@@ -164,6 +168,11 @@ typedef struct isd_seq_state {
  *      a = n: draw the bonus t from P_n and N-1 new drafts from rows
  *      n+1..n+N-1, next state FULL (n_draft = N-1, q_row = n+1).
  *   4. emit = (x_1..x_a, t), n_emit = kv_commit = a + 1.
+ * With proposal = ISD_PROPOSE_ARGMAX (the argmax proposal of the pages'
+ * serving stack, "Documentation et ressources > Serving (SGLang)") the new
+ * drafts are argmax of rows n+1..n+N-1 (ties to the smallest id) with
+ * q_x = 1, so step 2 reads u_j < P_{j-1}(x_j) and the residual of step 3 is
+ * P_a with x_{a+1} removed; prev_logits is then not read (may be NULL).
  * Draws are inverse-CDF over ascending token ids with u from Philox4x64-10:
  * key (seed, 0), counter (slot, b, step, 0), u = ((w0>>41) + 0.5) * 2^-23;
  * slots 1..N-1 test drafts, slot N draws t, slot N+k draws proposal k.
@@ -197,6 +206,8 @@ typedef struct isd_accept_args {
                          aligned, caller-owned, contents on entry ignored */
   size_t ws_bytes;
   int32_t* dev_err;
+  int32_t proposal;   /* ISD_PROPOSE_SAMPLE or ISD_PROPOSE_ARGMAX; the same on
+                         consecutive steps of a sequence */
 } isd_accept_args;
 
 size_t isd_accept_workspace_size(int C, int N, int V, int rows);

@@ -109,6 +109,9 @@ def test_accept_rejects_bad_arguments_on_host(lib):
     a.out = st_in
     assert lib.isd_accept(ctypes.byref(a), None) == -1  # out aliases in
     a.out = st_out
+    a.proposal = 7
+    assert lib.isd_accept(ctypes.byref(a), None) == -1  # unknown proposal rule
+    a.proposal = 0
     a.V, a.ld = 600000, 600000
     assert lib.isd_accept(ctypes.byref(a), None) == -2  # vocabulary beyond the cached chunk statistics
     assert lib.isd_accept_workspace_size(64, 4, 600000, 8) == 0

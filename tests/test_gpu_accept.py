@@ -28,8 +28,10 @@ class Trajectory:
     """Runs the GPU library and the oracle side by side, each on its own
     state, with logits from the same seeded generator."""
 
-    def __init__(self, seed, C, N, V, sigma_l, sigma_q, dtype, ctx0, steps, rows=None, ld=None):
+    def __init__(self, seed, C, N, V, sigma_l, sigma_q, dtype, ctx0, steps, rows=None, ld=None,
+                 proposal="sample"):
         self.seed, self.C, self.N, self.V = seed, C, N, V
+        self.proposal = proposal
         self.ld = ld or V
         self.R = rows or 2 * N
         self.gen = workload.TeacherLogits(seed, C, V, steps * N + self.R + 1, sigma_l, sigma_q, dtype)
@@ -61,7 +63,7 @@ class Trajectory:
             lg = padded
         lg = lg.to(DEV)
         out = dvd.isd_accept(lg, self.g_prev, self.g_in, self.g_out, N, self.seed, step, V=self.V,
-                             diag=True, dev_err=self.err)
+                             diag=True, dev_err=self.err, proposal=self.proposal)
         torch.cuda.synchronize()
         assert self.err.item() == 0
         g = {k: getattr(out, k).cpu().numpy() for k in
@@ -72,7 +74,7 @@ class Trajectory:
         lo = self.gen.block(step, self.o_ctx, self.ctx0, torch.from_numpy(self.o_n), self.R)
         lo64 = lo.double().numpy()
         u = philox.step_uniforms(self.seed, step, C, N)
-        o = ref.accept_step(lo64, self.o_prev, self.o_n, self.o_drafts, self.o_qrow, u, N)
+        o = ref.accept_step(lo64, self.o_prev, self.o_n, self.o_drafts, self.o_qrow, u, N, proposal=self.proposal)
         flags = ref.flagged(o, PROB_TOL)
 
         for b in np.flatnonzero(self.active):
@@ -349,3 +351,48 @@ def test_stride_sweep_tokens_per_forward(N, p):
           f"at the model's {chain.tpf_closed_form(N, p_model):.4f}", flush=True)
     assert abs(p_hat - p_model) <= 4 * p_se + 0.01
     assert abs(tpf - closed) <= 4 * se + 0.01
+
+
+# ---------------------------------------------- argmax proposals (a reading)
+
+def test_argmax_proposals_tiny_fp32():
+    """Drafts = argmax of the MASK rows, verified with u < P(x); fp32,
+    vocabulary 1024, 30 steps."""
+    t, acc = run_trajectory(30, seed=70, C=8, N=4, V=1024, sigma_l=2.0, sigma_q=0.3,
+                            dtype=torch.float32, ctx0=0, proposal="argmax")
+    assert t.excused <= 2
+
+
+def test_argmax_proposals_full_vocab_bf16():
+    t, _ = run_trajectory(4, seed=71, C=16, N=4, V=151936, sigma_l=3.0, sigma_q=0.25,
+                          dtype=torch.bfloat16, ctx0=100, proposal="argmax")
+    assert t.compared >= 4 * 16 - 4
+
+
+def test_argmax_first_emitted_token_follows_p_on_device():
+    """With a point-mass proposal the device still emits its first token
+    from P_0 (accept w.p. P(x), else P_0 without x): chi-square over 16 ids
+    and 16384 sequences."""
+    C, N, V, seed = 16384, 2, 16, 5
+    rng = np.random.default_rng(1)
+    P = rng.dirichlet(np.ones(V) * 0.8)
+    Q = rng.dirichlet(np.ones(V) * 0.8)
+    l0 = torch.zeros((C, 2 * N, V))
+    l0[:, 1] = torch.from_numpy(np.log(Q)).float()  # proposal row of the FRESH step
+    l1 = torch.zeros((C, 2 * N, V))
+    l1[:, 0] = torch.from_numpy(np.log(P)).float()  # verify row of draft 1
+    st0, st1, st2 = dvd.SeqState(C, N), dvd.SeqState(C, N), dvd.SeqState(C, N)
+    l0d, l1d = l0.to(DEV), l1.to(DEV)
+    dvd.isd_accept(l0d, None, st0, st1, N, seed, 0, V=V, proposal="argmax")
+    out = dvd.isd_accept(l1d, None, st1, st2, N, seed, 1, V=V, diag=True, proposal="argmax")
+    torch.cuda.synchronize()
+    assert (st1.drafts[:, 0].cpu().numpy() == int(np.argmax(Q))).all()
+    assert np.allclose(st1.q_x[:, 0].cpu().numpy(), 1.0)
+    first = out.emit[:, 0].cpu().numpy()
+    counts = np.bincount(first, minlength=V)
+    keep = P * C > 5
+    chi2, pval = stats.chisquare(counts[keep], P[keep] / P[keep].sum() * counts[keep].sum())
+    assert pval > 1e-4, (chi2, pval)
+    x = int(np.argmax(Q))
+    rej = out.accepted.cpu().numpy() == 0
+    assert np.allclose(out.resid_mass.cpu().numpy()[rej], 1.0 - P[x], atol=1e-5)
