@@ -304,7 +304,10 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--slices", type=int, default=0, help="attention workgroups per KV-head group (0 = automatic)")
+    ap.add_argument("--slices", type=int, default=-64,
+                    help="attention split: -T = batch-invariant chunks of T 32-key tiles (default: 64, the "
+                         "lossless R-ISD configuration); 0 = stream-K with automatic slices; S > 0 = stream-K "
+                         "with S workgroups per KV-head group")
     ap.add_argument("--proposal", choices=("sample", "argmax"), default="sample",
                     help="draft proposals: sampled from q (default) or argmax q")
     ap.add_argument("--copy-probe", action="store_true",
@@ -460,6 +463,8 @@ def main():
             "C": C, "N": N, "layers": L, "Hq": Hq, "Hkv": cfg["Hkv"], "head_dim": D, "vocab": V,
             "global_batch": C, "seq_len": int(np.mean(ctxs[W])), "parallelism": "none (1 GPU)",
             "proposal": cfg["proposal"],
+            "attention_split": ("batch-invariant, chunks of %d tiles" % -args.slices if args.slices < 0
+                                else "stream-K, %s slices" % (args.slices or "automatic")),
         },
         "roofline": {
             "kernel": "isd_attention (main + LSE merge launches of one call)",

@@ -174,6 +174,11 @@ def isd_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
     _check(rc, "isd_kv_write")
 
 
+def attn_invariant(chunk_tiles):
+    """`slices` value of the batch-invariant split (ISD_ATTN_INVARIANT)."""
+    return -int(chunk_tiles)
+
+
 def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, slices=0):
     s = kv.c_struct()
     return int(lib().isd_attention_workspace_size(C, rows, num_q_heads, ctypes.byref(s), max_len, slices))

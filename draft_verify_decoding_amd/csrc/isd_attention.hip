@@ -49,6 +49,8 @@ struct AttnParams {
   int C, rows, Hq, Hkv, group, M;
   int G;             // slices (workgroups) per KV-head group
   int MB, HPW;       // query blocks and KV heads per workgroup (one wave each)
+  int CT;            // > 0: batch-invariant split into chunks of CT tiles
+  int Kmax;          // chunks per sequence the workspace holds (CT > 0)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -208,6 +210,7 @@ struct AttnOps<float> {
 
 constexpr int kMaxSeqs = 8192;   // sequences per attention call (LDS prefix sums)
 constexpr int kTileBatch = 1024;  // tiles whose page ids are staged in LDS at once
+constexpr int kMaxChunkTiles = 1 << 16;  // largest chunk of the batch-invariant split
 
 template <typename E, int D>
 __device__ __forceinline__ const E* page_ptr(const void* pool, int pid, int Hkv, int g) {
@@ -224,7 +227,17 @@ __device__ __forceinline__ const E* page_ptr(const void* pool, int pid, int Hkv,
 // pieces of a sequence shared by several slices are written to two partial
 // slots per slice (its first and its last sequence) and merged afterwards in
 // slice order, so results do not depend on scheduling.
-template <typename E, int D>
+//
+// Batch-invariant split (CT > 0): each sequence is cut at fixed multiples of
+// CT tiles from position 0, and each chunk gets a workgroup of its own.
+// Pieces, their order and the merge then depend only on the sequence
+// itself, and a query column's arithmetic depends only on its own keys:
+// masked keys add exact zeros (exp2 of -inf), a rescale of a column
+// whose maximum did not move multiplies by exp2(0) = 1, and the MFMA result
+// of one column does not depend on the others. So a row of a block of rows
+// comes out bit for bit equal to the same query sent alone with ctx + row
+// cached tokens (the autoregressive forward), whatever else is in the batch.
+template <typename E, int D, bool kChunked>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   using Ops = AttnOps<E>;
   const int MB = p.MB;
@@ -233,11 +246,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int w = blockIdx.x % G;
   const int nthreads = 64 * p.HPW * MB;
 
-  // Tile offsets of the sequences (prefix sum), rebuilt by every workgroup.
+  // Tile offsets of the sequences (prefix sum, stream-K split only).
   __shared__ int s_off[kMaxSeqs + 1];
   __shared__ int s_part[512];
   __shared__ int s_pid[2 * kTileBatch];  // page ids of the current tile batch
-  {
+  int t_begin = 0, t_end = 0;
+  int u_first = 0;                   // first sequence of this workgroup
+  int c_nt = 0, c_units = 0, c_k = 0;  // chunked split: tiles, chunks, this chunk
+  if constexpr (kChunked) {
+    // workgroup w of a head group owns chunk w % Kmax of sequence w / Kmax;
+    // workgroups past the sequence's last chunk leave at once
+    u_first = w / p.Kmax;
+    c_k = w % p.Kmax;
+    const int ctx = p.ctx[u_first];
+    const bool reporter = c_k == 0 && hg == 0 && threadIdx.x == 0;
+    if (ctx < 0) {
+      if (reporter) set_dev_err(p.dev_err, ISD_DEV_STATE);
+      return;
+    }
+    c_nt = (ctx + p.rows + 31) / 32;
+    c_units = (c_nt + p.CT - 1) / p.CT;
+    if (c_units > p.Kmax) {  // ctx + rows beyond max_len: no room for its chunks
+      if (reporter) set_dev_err(p.dev_err, ISD_DEV_CAPACITY);
+      return;
+    }
+    if (c_k >= c_units) return;
+  } else {
     const int per = (p.C + nthreads - 1) / nthreads;
     const int b0 = threadIdx.x * per;
     int sum = 0;
@@ -265,15 +299,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     if (b0 < p.C && min(p.C, b0 + per) == p.C) s_off[p.C] = run;
     __syncthreads();
-  }
-  const long T = s_off[p.C];
-  const int t_begin = static_cast<int>(w * T / G);
-  const int t_end = static_cast<int>((w + 1) * T / G);
-  if (w == 0 && hg == 0)  // the merge launch reads the offsets back
-    for (int b = threadIdx.x; b <= p.C; b += nthreads) p.tile_off[b] = s_off[b];
-  if (t_begin >= t_end) return;
-  int u_first = 0;  // sequence holding tile t_begin
-  {
+    const long T = s_off[p.C];
+    t_begin = static_cast<int>(w * T / G);
+    t_end = static_cast<int>((w + 1) * T / G);
+    if (w == 0 && hg == 0)  // the merge launch reads the offsets back
+      for (int b = threadIdx.x; b <= p.C; b += nthreads) p.tile_off[b] = s_off[b];
+    if (t_begin >= t_end) return;
+    // sequence holding tile t_begin
     int lo = 0, hi = p.C - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) / 2;
@@ -303,9 +335,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   f32x16 o[D / 32];
   float m_run, l_run;
 
-  for (int b = u_first; b < p.C && s_off[b] < t_end; ++b) {
-    const int tb0 = s_off[b], tb1 = s_off[b + 1];
-    const int lt0 = max(t_begin, tb0) - tb0, lt1 = min(t_end, tb1) - tb0;
+  // Pieces: the slice's share of each sequence it touches (stream-K), or
+  // the workgroup's one chunk (chunked split).
+  for (int b = u_first; kChunked ? b == u_first : (b < p.C && s_off[b] < t_end); ++b) {
+    int nt, k = 0, tb0 = 0;
+    if constexpr (kChunked) {
+      nt = c_nt;
+      k = c_k;
+    } else {
+      tb0 = s_off[b];
+      nt = s_off[b + 1] - tb0;
+    }
+    const int lt0 = kChunked ? k * p.CT : max(t_begin, tb0) - tb0;
+    const int lt1 = kChunked ? min(nt, lt0 + p.CT) : min(t_end, tb0 + nt) - tb0;
     if (lt0 >= lt1) continue;
     const int ctx = p.ctx[b];
     const int L = ctx + p.rows;  // positions 0 .. L-1 are read
@@ -448,7 +490,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     // block nb holds dim 32nb + 8(e/4) + 4hh + e%4: four registers make one
     // 16-byte store.
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
-    const bool whole = lt0 == 0 && lt1 == tb1 - tb0;
+    const bool whole = kChunked ? c_units == 1 : lt0 == 0 && lt1 == nt;
     if (qvalid) {
       float* dst;
       float mul;
@@ -456,8 +498,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         dst = p.out + ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
         mul = 1.f / l_tot;
       } else {
-        const int slot = (b == u_first) ? 0 : 1;
-        const size_t idx = ((static_cast<size_t>(hg * G + w) * 2 + slot) * (p.HPW * MB) + hl_w * MB + rb) * 32 + lane32;
+        // partial piece of this wave's query columns
+        const size_t pidx =
+            kChunked ? ((static_cast<size_t>(b) * p.Kmax + k) * (p.Hkv / p.HPW) + hg) * (p.HPW * MB) + hl_w * MB + rb
+                     : (static_cast<size_t>(hg * G + w) * 2 + (b == u_first ? 0 : 1)) * (p.HPW * MB) + hl_w * MB + rb;
+        const size_t idx = pidx * 32 + lane32;
         dst = p.part_o + idx * D;
         mul = 1.f;
         if (hh == 0) {
@@ -492,39 +537,57 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   const int qb = blockIdx.y;
   const int G = p.G;
   const int hg = g / p.HPW, hl_w = g % p.HPW;
-  const long T = p.tile_off[p.C];
-  const int tb0 = p.tile_off[b], tb1 = p.tile_off[b + 1];
-  if (tb1 <= tb0 || T == 0) return;
-  // slice holding tile x: the largest w with floor(w*T/G) <= x
-  auto slice_of = [&](long x) { return static_cast<int>(((x + 1) * G + T - 1) / T - 1); };
-  const int wa = slice_of(tb0), wb = slice_of(tb1 - 1);
-  if (wa == wb) return;  // finalised by its slice
+  // Pieces j = 0 .. n-1 of the sequence, in order: its slices wa .. wb
+  // (stream-K split) or its chunks (chunked split).
+  long T = 0;
+  int tb0 = 0, wa = 0, n;
+  if (p.CT > 0) {
+    const int ctx = p.ctx[b];
+    if (ctx < 0) return;
+    n = ((ctx + p.rows + 31) / 32 + p.CT - 1) / p.CT;
+    if (n > p.Kmax) return;  // not computed (flagged by the main launch)
+  } else {
+    T = p.tile_off[p.C];
+    tb0 = p.tile_off[b];
+    const int tb1 = p.tile_off[b + 1];
+    if (tb1 <= tb0 || T == 0) return;
+    // slice holding tile x: the largest w with floor(w*T/G) <= x
+    auto slice_of = [&](long x) { return static_cast<int>(((x + 1) * G + T - 1) / T - 1); };
+    wa = slice_of(tb0);
+    n = slice_of(tb1 - 1) - wa + 1;
+  }
+  if (n == 1) return;  // finalised by the main launch
   constexpr int kDimsPerThread = D * 32 / 256;
   constexpr int kV = kDimsPerThread / 4;
   constexpr int kBatch = 8;
   const int col = qb * 32 + threadIdx.x / (256 / 32);
   const int d0 = (threadIdx.x % (256 / 32)) * kDimsPerThread;
   if (col >= p.M) return;
-  auto piece = [&](int w2) {
-    const long start = w2 * T / G;
-    const int slot = start >= tb0 ? 0 : 1;
-    return ((static_cast<size_t>(hg * G + w2) * 2 + slot) * (p.HPW * MB) + hl_w * MB + qb) * 32 + (col - qb * 32);
+  auto piece = [&](int j) {
+    size_t pidx;
+    if (p.CT > 0) {
+      pidx = ((static_cast<size_t>(b) * p.Kmax + j) * (p.Hkv / p.HPW) + hg) * (p.HPW * MB) + hl_w * MB + qb;
+    } else {
+      const int w2 = wa + j;
+      const int slot = (w2 * T / G) >= tb0 ? 0 : 1;
+      pidx = (static_cast<size_t>(hg * G + w2) * 2 + slot) * (p.HPW * MB) + hl_w * MB + qb;
+    }
+    return pidx * 32 + (col - qb * 32);
   };
   // a slice whose range is empty (more slices than tiles) holds no piece
-  auto empty = [&](int w2) { return (w2 * T / G) == ((w2 + 1) * T / G); };
+  auto empty = [&](int j) { return p.CT <= 0 && ((wa + j) * T / G) == ((wa + j + 1) * T / G); };
   float m_run = -1e30f, l_run = 0.f;  // finite floor: exp2(m_run - m_new) stays defined
   f32x4 acc[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int w0 = wa; w0 <= wb; w0 += kBatch) {
+  for (int j0 = 0; j0 < n; j0 += kBatch) {
     float mv[kBatch], lv[kBatch];
     f32x4 ov[kBatch][kV];
     bool has[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int w2 = w0 + j;
-      has[j] = w2 <= wb && !empty(w2);
-      const size_t idx = piece(has[j] ? w2 : wa);  // slice wa holds a piece
+      has[j] = j0 + j < n && !empty(j0 + j);
+      const size_t idx = piece(has[j] ? j0 + j : 0);  // piece 0 always exists
       mv[j] = p.part_ml[idx * 2];
       lv[j] = p.part_ml[idx * 2 + 1];
       const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
@@ -624,6 +687,7 @@ int check_kv(const isd_kv_cache* kv) {
 
 struct AttnPlan {
   int MB, HPW, groups, G;
+  int CT, Kmax;  // batch-invariant split (CT > 0): chunk tiles, chunks per sequence
   size_t off_bytes, part_o_bytes, part_ml_bytes;
   size_t total() const { return off_bytes + part_o_bytes + part_ml_bytes; }
 };
@@ -636,7 +700,7 @@ int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len,
   const int M = (Hq / Hkv) * rows;
   if (M > 128) return ISD_E_UNSUPPORTED;
   if (max_len < rows) return ISD_E_INVALID;
-  if (slices < 0) return ISD_E_INVALID;
+  if (slices < -kMaxChunkTiles) return ISD_E_INVALID;
   plan->MB = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   // KV heads per workgroup: the largest power of two that divides Hkv with
   // at most 8 waves (one per head and query block) in the workgroup.
@@ -645,12 +709,28 @@ int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len,
   plan->groups = Hkv / plan->HPW;
   // Default: 2048 waves over the chip (8 per CU: the register-file limit of
   // this kernel), spread over the head groups; never more slices than tiles.
-  long G = slices ? slices : std::max(1, 2048 / (plan->HPW * plan->MB) / plan->groups);
+  const long auto_G = std::max(1, 2048 / (plan->HPW * plan->MB) / plan->groups);
   const long max_tiles = static_cast<long>(C) * ((max_len + 31) / 32);
-  if (G > max_tiles) G = std::max(1L, max_tiles);
-  plan->G = static_cast<int>(G);
+  size_t pieces;  // partial (query block, KV head) pieces the workspace holds
+  if (slices < 0) {
+    // batch-invariant split: one workgroup per (head group, sequence, chunk
+    // of CT tiles), so the hardware dispatcher balances the chunks
+    plan->CT = -slices;
+    plan->Kmax = static_cast<int>(((max_len + 31) / 32 + plan->CT - 1) / plan->CT);
+    const long G = static_cast<long>(C) * plan->Kmax;
+    if (G * Hkv > INT_MAX) return ISD_E_UNSUPPORTED;  // grid size
+    plan->G = static_cast<int>(std::max(1L, G));
+    pieces = static_cast<size_t>(C) * plan->Kmax;
+  } else {
+    plan->CT = 0;
+    plan->Kmax = 0;
+    long G = slices ? slices : auto_G;
+    if (G > max_tiles) G = std::max(1L, max_tiles);
+    plan->G = static_cast<int>(G);
+    pieces = static_cast<size_t>(plan->G) * 2;
+  }
+  pieces *= static_cast<size_t>(plan->groups) * plan->HPW * plan->MB * 32;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t pieces = static_cast<size_t>(plan->groups) * plan->G * 2 * plan->HPW * plan->MB * 32;
   plan->off_bytes = up(static_cast<size_t>(C + 1) * sizeof(int32_t));
   plan->part_o_bytes = up(pieces * kv->head_dim * sizeof(float));
   plan->part_ml_bytes = up(pieces * 2 * sizeof(float));
@@ -659,8 +739,12 @@ int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len,
 
 template <typename E, int D>
 hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((attention_kernel<E, D>), dim3(static_cast<unsigned>(groups * p.G)),
-                     dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
+  if (p.CT > 0)
+    hipLaunchKernelGGL((attention_kernel<E, D, true>), dim3(static_cast<unsigned>(groups * p.G)),
+                       dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attention_kernel<E, D, false>), dim3(static_cast<unsigned>(groups * p.G)),
+                       dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
   hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(p.MB)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -717,6 +801,8 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   p.G = plan.G;
   p.MB = plan.MB;
   p.HPW = plan.HPW;
+  p.CT = plan.CT;
+  p.Kmax = plan.Kmax;
   p.scale_log2 = scale * kLog2e;
 
   hipError_t e;

@@ -122,16 +122,33 @@ int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
  *   ctx  [C] cached tokens before the block
  *   Query head h reads KV head h / (Hq / Hkv). scale multiplies q.k
  *   (1/sqrt(D) in the usual model). max_len is a host-side upper bound of
- *   ctx[b] + rows, used only to size the launch (results do not depend on
- *   it). The 32-key tiles of all sequences are split evenly over `slices`
- *   workgroups per group of KV heads (0 = automatic: one per CU for 8B and
- *   32B shapes); sequences shared by several workgroups are merged with a
- *   log-sum-exp combine in a fixed order, so results do not depend on
- *   scheduling. The workspace (size from isd_attention_workspace_size with
- *   the same arguments) holds those partial results; no initialisation.
+ *   ctx[b] + rows, used to size the launch and the workspace. The 32-key
+ *   tiles of all sequences are split evenly over `slices` workgroups per
+ *   group of KV heads (0 = automatic: one per CU for 8B and 32B shapes);
+ *   sequences shared by several workgroups are merged with a log-sum-exp
+ *   combine in a fixed order, so results do not depend on scheduling (but
+ *   do depend on the rest of the batch, through the split).
+ *   slices = ISD_ATTN_INVARIANT(t), 1 <= t <= 65536, selects the
+ *   batch-invariant split instead: every sequence is cut into chunks of t
+ *   tiles (32t keys) from position 0, one workgroup per chunk (it runs
+ *   best while a call's chunks do not outnumber the CUs), merged in chunk
+ *   order. Then row i of sequence b is bit for bit equal to the same query
+ *   sent as a one-row call with ctx[b] + i cached tokens and the same t, in
+ *   any batch: the
+ *   reduction order of the clean rows of a stride block is that of the
+ *   autoregressive forward, which the bit-identical output of lossless
+ *   R-ISD needs (I-DLM page, "Speedup Factor Explorer" and "Documentation
+ *   et ressources > Lossless R-ISD"). In this mode ctx[b] + rows must not
+ *   exceed max_len: a sequence that does is left unwritten and flags
+ *   ISD_DEV_CAPACITY.
+ *   The workspace (size from isd_attention_workspace_size with the same
+ *   arguments) holds the partial results; no initialisation.
  * Supported: D in {64, 128}; Hq multiple of Hkv; (Hq/Hkv)*rows <= 128;
- * rows <= 64; C <= 8192.
+ * rows <= 64; C <= 8192; in the batch-invariant split also
+ * C * ceil(ceil(max_len / 32) / t) * Hkv <= INT_MAX (else
+ * ISD_E_UNSUPPORTED).
  */
+#define ISD_ATTN_INVARIANT(chunk_tiles) (-(chunk_tiles))
 size_t isd_attention_workspace_size(int C, int rows, int num_q_heads,
                                     const isd_kv_cache* kv, int max_len,
                                     int slices);

@@ -64,9 +64,10 @@ def test_attention_rejects_bad_arguments_on_host(lib):
     kv.num_kv_heads = 1
     # group * rows > 128
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 40, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
-    # scale must be positive, slices >= 0, max_len >= rows
+    # scale must be positive, chunks of the invariant split <= 65536 tiles, max_len >= rows
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, -1.0, 64, 0, 16, None, 0, None, None) == -1
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -3, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -65537, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -3, 16, None, 0, None, None) == -3
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4, 0, 16, None, 0, None, None) == -1
     # misaligned q
     assert lib.isd_attention(ctypes.byref(kv), 18, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -1
@@ -78,6 +79,24 @@ def test_attention_rejects_bad_arguments_on_host(lib):
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, None, 0, None, None) == -3
     assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, 1 << 20, need - 16, None,
                              None) == -3
+
+
+def test_attention_invariant_split_workspace(lib):
+    """Chunked split: one partial piece per (sequence, chunk, KV head, query
+    block), C * ceil(ceil(max_len / 32) / t) chunks, whatever the slices."""
+    kv = dvd.IsdKvCache(16, 16, 16, 4, 10, 16, 8, 128, dvd.ISD_BF16)
+    C, rows, Hq, max_len = 64, 8, 32, 8200
+    for t in (1, 16, 64, 300):
+        chunks = C * -(-(-(-max_len // 32)) // t)
+        pieces = chunks * 8 * 1 * 32  # 8 KV heads, one 32-column query block (4 x 8 rows)
+        off = -(-(C + 1) * 4 // 256) * 256
+        want = off + -(-pieces * 128 * 4 // 256) * 256 + -(-pieces * 2 * 4 // 256) * 256
+        assert lib.isd_attention_workspace_size(C, rows, Hq, ctypes.byref(kv), max_len,
+                                                dvd.attn_invariant(t)) == want
+    assert lib.isd_attention_workspace_size(C, rows, Hq, ctypes.byref(kv), max_len, -70000) == 0
+    # one workgroup per chunk: C * chunks * Hkv must fit the grid
+    assert lib.isd_attention_workspace_size(8192, rows, Hq, ctypes.byref(kv), 1 << 20, -1) == 0
+    assert lib.isd_attention_workspace_size(8192, rows, Hq, ctypes.byref(kv), 1 << 20, -2) > 0
 
 
 def test_kv_write_rejects_bad_arguments_on_host(lib):

@@ -5,6 +5,8 @@ inputs, fp32 accumulation), read normwise per (sequence, query head) slab:
 max |O - O*| / max |O*| over its rows x D. fp32 inputs are held to 1e-5.
 """
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -169,3 +171,73 @@ def test_32b_stride_sweep_shapes(N):
     case = workload.AttentionCase(50 + N, C=16, rows=2 * N, Hq=64, Hkv=8, D=128, ctx=16384)
     got, want = run(case, seqs=np.array([3, 12]))
     assert slab_errors(got, want).max() < 2e-3
+
+
+def bits(t):
+    return t.contiguous().view(-1).view(torch.int32)
+
+
+@pytest.mark.parametrize("t,Hq,dtype", [(1, 32, torch.bfloat16), (4, 32, torch.bfloat16),
+                                         (4, 64, torch.bfloat16), (64, 32, torch.bfloat16),
+                                         (4, 32, torch.float32)])
+def test_invariant_split_rows_equal_one_row_calls(t, Hq, dtype):
+    """Batch-invariant split: row i of every stride block equals, bit for bit,
+    the same query sent as a one-row call with ctx + i cached tokens (the AR
+    forward), whether those calls are batched together, reordered, or one
+    sequence alone. Contexts put blocks across chunk boundaries (32t - 3),
+    on them (32t), and make sequences of many chunks."""
+    C, rows, D = 7, 8, 128
+    ctx = [0, 5, 32 * t - 3, 32 * t, 3 * 32 * t - 1, 700, 2100]
+    case = workload.AttentionCase(41 + t, C=C, rows=rows, Hq=Hq, Hkv=8, D=D, ctx=ctx, dtype=dtype)
+    print(f"invariant split t={t} Hq={Hq} {dtype} ctx={ctx}", flush=True)
+    kv, err = fill_cache(case)
+    max_len = int(case.lengths.max())
+    ctx_d = torch.from_numpy(case.ctx).to(DEV)
+    q = case.q.to(DEV)
+    inv = dvd.attn_invariant(t)
+    blk = dvd.isd_attention(kv, q, ctx_d, max_len=max_len, slices=inv, dev_err=err)
+
+    # every row as its own one-row sequence over its sequence's pages
+    ar = copy.copy(kv)
+    ar.block_table = kv.block_table.repeat_interleave(rows, dim=0).contiguous()
+    ctx1 = (ctx_d[:, None] + torch.arange(rows, device=DEV, dtype=torch.int32)[None, :]).reshape(-1).contiguous()
+    q1 = q.reshape(C * rows, 1, Hq, D).contiguous()
+    one = dvd.isd_attention(ar, q1, ctx1, max_len=max_len, slices=inv, dev_err=err)
+    # the same one-row calls in reverse order, with a larger max_len
+    rev = torch.arange(C * rows - 1, -1, -1, device=DEV)
+    ar_r = copy.copy(kv)
+    ar_r.block_table = ar.block_table[rev].contiguous()
+    one_r = dvd.isd_attention(ar_r, q1[rev].contiguous(), ctx1[rev].contiguous(), max_len=max_len + 500,
+                              slices=inv, dev_err=err)
+    # the longest sequence alone, as a block
+    solo_kv = copy.copy(kv)
+    solo_kv.block_table = kv.block_table[C - 1:].contiguous()
+    solo = dvd.isd_attention(solo_kv, q[C - 1:].contiguous(), ctx_d[C - 1:].contiguous(), max_len=max_len,
+                             slices=inv, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(blk), bits(one))
+    assert torch.equal(bits(one_r), bits(one[rev]))
+    assert torch.equal(bits(solo), bits(blk[C - 1:]))
+    # and it is the attention the oracle computes
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q), kp, vp, case.table, case.ctx)
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert slab_errors(blk.cpu().double().numpy(), want).max() < tol
+
+
+def test_invariant_split_flags_sequences_beyond_max_len():
+    """Chunked split with max_len below a sequence's length: that sequence is
+    left unwritten and ISD_DEV_CAPACITY is flagged; the others are exact."""
+    case = workload.AttentionCase(47, C=3, rows=8, Hq=8, Hkv=2, D=64, ctx=[0, 100, 500])
+    kv, err = fill_cache(case)
+    out = torch.full((3, 8, 8, 64), 7.0, device=DEV)
+    dvd.isd_attention(kv, case.q.to(DEV), torch.from_numpy(case.ctx).to(DEV), max_len=120,
+                      slices=dvd.attn_invariant(2), out=out, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 2  # ISD_DEV_CAPACITY
+    got = out.cpu().double().numpy()
+    assert (got[2] == 7.0).all()
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q[:2]), kp, vp, case.table[:2], case.ctx[:2])
+    assert slab_errors(got[:2], want).max() < 2e-3
