@@ -124,7 +124,8 @@ int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
  *   (1/sqrt(D) in the usual model). max_len is a host-side upper bound of
  *   ctx[b] + rows, used to size the launch and the workspace. The 32-key
  *   tiles of all sequences are split evenly over `slices` workgroups per
- *   group of KV heads (0 = automatic: one per CU for 8B and 32B shapes);
+ *   group of KV heads (0 = automatic: 1536 waves over the chip, i.e. a
+ *   workgroup on three CUs in four for 8B and 32B shapes);
  *   sequences shared by several workgroups are merged with a log-sum-exp
  *   combine in a fixed order, so results do not depend on scheduling (but
  *   do depend on the rest of the batch, through the split).
