@@ -88,6 +88,10 @@ _SIGNATURES = {
                                      ctypes.c_void_p, ctypes.c_void_p]),
     "isd_accept_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "isd_accept": (ctypes.c_int, [ctypes.POINTER(IsdAcceptArgs), ctypes.c_void_p]),
+    "isd_block_assemble": (ctypes.c_int, [ctypes.POINTER(IsdSeqState), ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]),
     "isd_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.c_void_p]),
     "isd_lora_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int]),
@@ -278,6 +282,27 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     args.proposal = PROPOSE[proposal]
     _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
     return out
+
+
+def isd_block_assemble(state, emit, n_emit, ctx, N, mask_id, tokens=None, positions=None, is_mask=None,
+                       dev_err=None, stream=None):
+    """The next step's block [C, 2N] from the state and outputs isd_accept
+    wrote: newest emitted token, pending drafts, MASK rows. Returns
+    (tokens, positions, is_mask); positions and is_mask are made when ctx is
+    given or when passed in."""
+    C = emit.shape[0]
+    dev = emit.device
+    if tokens is None:
+        tokens = torch.empty((C, 2 * N), dtype=torch.int32, device=dev)
+    if positions is None and ctx is not None:
+        positions = torch.empty((C, 2 * N), dtype=torch.int32, device=dev)
+    if is_mask is None:
+        is_mask = torch.empty((C, 2 * N), dtype=torch.uint8, device=dev)
+    s = state.c_struct()
+    _check(lib().isd_block_assemble(ctypes.byref(s), _p(emit), _p(n_emit), _p(ctx), C, N, int(mask_id), _p(tokens),
+                                    _p(positions), _p(is_mask), _p(dev_err), _stream(stream)),
+           "isd_block_assemble")
+    return tokens, positions, is_mask
 
 
 # --------------------------------------------------------------- projections

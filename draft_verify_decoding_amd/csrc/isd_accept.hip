@@ -662,6 +662,38 @@ __global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p)
   finish<E>(p, b, d);
 }
 
+// ----------------------------------------------------------- block assembly
+// The next step's stride block: row 0 is the newest emitted token (the bonus
+// or the resampled one, at position ctx after the commit), rows 1..n the n
+// pending drafts, the rest MASK. One thread per (sequence, row).
+__global__ __launch_bounds__(256) void block_assemble_kernel(const int32_t* n_draft, const int32_t* drafts,
+                                                             const int32_t* emit, const int32_t* n_emit,
+                                                             const int32_t* ctx, int C, int N, int32_t mask_id,
+                                                             int32_t* tokens, int32_t* positions, uint8_t* is_mask,
+                                                             int32_t* dev_err) {
+  const int R = 2 * N;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= C * R) return;
+  const int b = idx / R, i = idx % R;
+  const int n = n_draft[b], ne = n_emit[b];
+  const bool ok = (n == 0 || n == N - 1) && ne >= 1 && ne <= N;
+  int32_t tok = -1;
+  bool masked = false;
+  if (!ok) {
+    if (i == 0) set_dev_err(dev_err, ISD_DEV_STATE);
+  } else if (i == 0) {
+    tok = emit[static_cast<long>(b) * N + ne - 1];
+  } else if (i <= n) {
+    tok = drafts[static_cast<long>(b) * (N - 1) + i - 1];
+  } else {
+    tok = mask_id;
+    masked = true;
+  }
+  tokens[idx] = tok;
+  if (is_mask) is_mask[idx] = masked ? 1 : 0;
+  if (positions) positions[idx] = ctx[b] + i;
+}
+
 }  // namespace isd
 
 // ================================================================ host API
@@ -764,6 +796,23 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.dev_err = a->dev_err;
   const hipError_t e = a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, stream) : launch_accept<float>(p, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+}
+
+int isd_block_assemble(const isd_seq_state* st, const int32_t* emit, const int32_t* n_emit, const int32_t* ctx,
+                       int C, int N, int32_t mask_id, int32_t* tokens, int32_t* positions, uint8_t* is_mask,
+                       int32_t* dev_err, hipStream_t stream) {
+  if (!st || C < 0 || N < 2) return ISD_E_INVALID;
+  if (N > kMaxN) return ISD_E_UNSUPPORTED;
+  if (C == 0) return ISD_OK;
+  if (!st->n_draft || !st->drafts || !emit || !n_emit || !tokens) return ISD_E_INVALID;
+  if (positions && !ctx) return ISD_E_INVALID;
+  if (static_cast<long>(C) * 2 * N > INT_MAX) return ISD_E_UNSUPPORTED;
+  const int rc = isd_check_device_internal();
+  if (rc) return rc;
+  const int total = C * 2 * N;
+  hipLaunchKernelGGL(block_assemble_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, st->n_draft, st->drafts,
+                     emit, n_emit, ctx, C, N, mask_id, tokens, positions, is_mask, dev_err);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
 }  // extern "C"

@@ -12,6 +12,7 @@
  *   isd_kv_write      put the block's K/V rows into the paged cache
  *   isd_attention     causal GQA attention of the block over the pages
  *   isd_accept        vocab softmax, p/q test, residual / bonus draw, proposals
+ *   isd_block_assemble  the next step's block: newest token, drafts, MASK
  *   isd_linear        y = x W^T (bf16 in, fp32 out), the base projection
  *   gated_lora_apply  y += s (x A^T) B^T on MASK rows only (R-ISD)
  *   isd_linear_gated  both of the above in one pass
@@ -230,6 +231,33 @@ typedef struct isd_accept_args {
 
 size_t isd_accept_workspace_size(int C, int N, int V, int rows);
 int isd_accept(const isd_accept_args* args, hipStream_t stream);
+
+/* Block assembly: the stride block of the next step, from the state and
+ * outputs isd_accept just wrote (I-DLM page, "Methodologie d'I-DLM >
+ * Introspective Strided Decoding (ISD)": one forward carries the clean
+ * tokens to verify and MASK positions for the next proposals). Row 0 is
+ * the newest emitted token emit[b][n_emit[b] - 1] (not yet in the cache),
+ * rows 1..n are the n = st->n_draft[b] pending drafts, the other rows of
+ * the 2N are mask_id:
+ *   FULL  (n = N-1): [t, d_1 .. d_{N-1}, MASK x N]
+ *   FRESH (n = 0):   [t, MASK x (2N-1)]
+ * Row i sits at position ctx[b] + i (ctx after the commit).
+ *   st        the state isd_accept wrote (n_draft, drafts read)
+ *   emit      [C][N], n_emit [C] from the same isd_accept call
+ *   ctx       [C]; may be NULL when positions is NULL
+ *   tokens    [C][2N] int32 out
+ *   positions [C][2N] int32 out, optional (NULL: not written)
+ *   is_mask   [C][2N] uint8 out, optional: 1 on MASK rows (the gated LoRA's
+ *             mask for the block), 0 elsewhere
+ * A sequence whose step was not taken (n_emit outside 1..N) or whose state
+ * is neither FULL nor FRESH gets tokens -1, is_mask 0 and ISD_DEV_STATE.
+ * Supported: 2 <= N <= 8. Errors: ISD_E_INVALID for a missing pointer.
+ */
+int isd_block_assemble(const isd_seq_state* st, const int32_t* emit,
+                       const int32_t* n_emit, const int32_t* ctx, int C,
+                       int N, int32_t mask_id, int32_t* tokens,
+                       int32_t* positions, uint8_t* is_mask,
+                       int32_t* dev_err, hipStream_t stream);
 
 /* ------------------------------------------------------ projections
  * Base projection of the model and the gated LoRA of lossless R-ISD

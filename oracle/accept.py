@@ -197,3 +197,40 @@ def flagged(out, tol=1e-5):
         if np.any(pm[np.isfinite(pm)] < tol):
             flag[b] = True
     return flag
+
+
+def block_assemble(n_draft, drafts, emit, n_emit, ctx, N, mask_id):
+    """The next step's stride block of every sequence (I-DLM,
+    fr.news.hada.io, "Méthodologie d'I-DLM > Introspective Strided Decoding
+    (ISD)": each forward carries the clean tokens still to be verified and
+    MASK positions for the next proposals).
+
+    Reading (the block layout above): row 0 is the last token the step
+    emitted (the bonus or the resampled token, not yet in the KV cache),
+    rows 1..n are the n pending drafts, the other rows of the 2N are MASK:
+    FULL (n = N-1) gives [t, d_1..d_{N-1}, MASK x N], FRESH (n = 0) gives
+    [t, MASK x (2N-1)]. Row i sits at position ctx + i, with ctx taken after
+    the commit. A sequence whose step was not taken (n_emit < 1) or whose
+    state is not FULL or FRESH gets -1 tokens and no MASK rows.
+
+    n_draft [C], drafts [C, N-1], emit [C, N], n_emit [C], ctx [C] (ints)
+    Returns tokens [C, 2N], positions [C, 2N], is_mask [C, 2N] (bool).
+    """
+    C = len(n_draft)
+    R = 2 * N
+    tokens = np.full((C, R), -1, np.int64)
+    positions = np.zeros((C, R), np.int64)
+    is_mask = np.zeros((C, R), bool)
+    for b in range(C):
+        positions[b] = int(ctx[b]) + np.arange(R)
+        n, ne = int(n_draft[b]), int(n_emit[b])
+        if n not in (0, N - 1) or not 1 <= ne <= N:
+            continue
+        tokens[b, 0] = emit[b][ne - 1]
+        for i in range(1, R):
+            if i <= n:
+                tokens[b, i] = drafts[b][i - 1]
+            else:
+                tokens[b, i] = mask_id
+                is_mask[b, i] = True
+    return tokens, positions, is_mask

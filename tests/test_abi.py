@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_expected_calls():
     names = declared_functions()
     for n in ["isd_kv_write", "isd_attention", "isd_attention_workspace_size", "isd_accept",
-              "isd_accept_workspace_size", "isd_linear", "gated_lora_apply", "isd_linear_gated",
+              "isd_accept_workspace_size", "isd_block_assemble", "isd_linear", "gated_lora_apply", "isd_linear_gated",
               "isd_lora_workspace_size", "isd_strerror", "isd_version"]:
         assert n in names, n
 
@@ -146,3 +146,15 @@ def test_linear_rejects_bad_arguments_on_host(lib):
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 16, 8, None) == -3  # ws too small
     assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4 * 9  # 8 split-K partials of U, then U
     assert lib.gated_lora_apply(16, 16, 24, 16, 4, 64, 8, 32, 1.0, 16, 16, 512, None) == -1  # B misaligned
+
+
+def test_block_assemble_rejects_bad_arguments_on_host(lib):
+    st = dvd.IsdSeqState(16, 16, 16, 16, 16, 16)
+    f = lib.isd_block_assemble
+    assert f(None, 16, 16, 16, 4, 4, 7, 16, 16, 16, None, None) == -1          # no state
+    assert f(ctypes.byref(st), 16, 16, 16, 0, 4, 7, 16, 16, 16, None, None) == 0  # nothing to do
+    assert f(ctypes.byref(st), 16, 16, 16, 4, 1, 7, 16, 16, 16, None, None) == -1  # N < 2
+    assert f(ctypes.byref(st), 16, 16, 16, 4, 9, 7, 16, 16, 16, None, None) == -2  # N > 8
+    assert f(ctypes.byref(st), 16, 16, 16, 4, 4, 7, None, 16, 16, None, None) == -1  # no tokens
+    assert f(ctypes.byref(st), None, 16, 16, 4, 4, 7, 16, 16, 16, None, None) == -1  # no emit
+    assert f(ctypes.byref(st), 16, 16, None, 4, 4, 7, 16, 16, 16, None, None) == -1  # positions need ctx

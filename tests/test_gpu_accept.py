@@ -90,6 +90,21 @@ class Trajectory:
             self.compared += 1
             self.flagged_agree += int(flags[b])
 
+        # the next step's block, assembled on the device from the device's
+        # outputs and by the oracle from its own: equal on every sequence
+        # still compared
+        g_ctx_next = (self.g_ctx + torch.from_numpy(g["kv_commit"]).long()).to(torch.int32).to(DEV)
+        tok, pos, msk = dvd.isd_block_assemble(self.g_out, out.emit, out.n_emit, g_ctx_next, N, self.V,
+                                               dev_err=self.err)
+        torch.cuda.synchronize()
+        assert self.err.item() == 0
+        o_tok, o_pos, o_msk = ref.block_assemble(o["n_draft_next"], o["drafts_next"], o["emit"], o["n_emit"],
+                                                 self.o_ctx.numpy() + o["kv_commit"], N, self.V)
+        act = self.active
+        assert np.array_equal(tok.cpu().numpy()[act], o_tok[act])
+        assert np.array_equal(pos.cpu().numpy()[act], o_pos[act])
+        assert np.array_equal(msk.cpu().numpy()[act].astype(bool), o_msk[act])
+
         # advance both sides
         self.g_ctx += torch.from_numpy(g["kv_commit"]).long()
         self.g_in, self.g_out = self.g_out, self.g_in
@@ -396,3 +411,33 @@ def test_argmax_first_emitted_token_follows_p_on_device():
     x = int(np.argmax(Q))
     rej = out.accepted.cpu().numpy() == 0
     assert np.allclose(out.resid_mass.cpu().numpy()[rej], 1.0 - P[x], atol=1e-5)
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 8])
+def test_block_assemble_matches_oracle(N):
+    """Block assembly on synthetic states and step outputs (5% invalid):
+    tokens, positions and mask bit-exact against the oracle; invalid
+    sequences flagged with ISD_DEV_STATE."""
+    C, V, mask_id = 3000, 151936, 151669
+    print(f"block assemble C={C} N={N}", flush=True)
+    for bad_frac in (0.0, 0.05):
+        n_draft, drafts, emit, n_emit, ctx = workload.step_outputs(N, C, N, V, bad_frac)
+        st = dvd.SeqState(C, N)
+        st.n_draft.copy_(torch.from_numpy(n_draft))
+        st.drafts.copy_(torch.from_numpy(drafts))
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        tok, pos, msk = dvd.isd_block_assemble(st, torch.from_numpy(emit).to(DEV), torch.from_numpy(n_emit).to(DEV),
+                                               torch.from_numpy(ctx).to(DEV), N, mask_id, dev_err=err)
+        torch.cuda.synchronize()
+        o_tok, o_pos, o_msk = ref.block_assemble(n_draft, drafts, emit, n_emit, ctx, N, mask_id)
+        assert np.array_equal(tok.cpu().numpy(), o_tok)
+        assert np.array_equal(pos.cpu().numpy(), o_pos)
+        assert np.array_equal(msk.cpu().numpy().astype(bool), o_msk)
+        invalid = (o_tok[:, 0] == -1).any()
+        assert err.item() == (16 if invalid else 0)
+        assert invalid == (bad_frac > 0)
+    # tokens only: positions and mask are optional
+    tok2, pos2, msk2 = dvd.isd_block_assemble(st, torch.from_numpy(emit).to(DEV), torch.from_numpy(n_emit).to(DEV),
+                                              None, N, mask_id, is_mask=None)
+    torch.cuda.synchronize()
+    assert pos2 is None and np.array_equal(tok2.cpu().numpy(), o_tok)

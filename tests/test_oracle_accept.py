@@ -342,3 +342,81 @@ def test_argmax_loop_reproduces_closed_form():
         n, drafts, q_row, prev = out["n_draft_next"], out["drafts_next"], out["q_row_next"], cur
     tpf = tokens / (C * steps)
     assert abs(tpf - chain.tpf_closed_form(N, p)) < 0.08, tpf
+
+
+# ------------------------------------------------------------ block assembly
+
+MASK = 151669  # any id outside the synthetic vocabularies below
+
+
+def test_block_assemble_layout_examples():
+    """The stride block layout (the FULL/FRESH reading): written out by hand
+    for N = 4 and N = 2, not computed."""
+    N = 4
+    tokens, pos, is_mask = accept.block_assemble(
+        n_draft=[3, 0, 3], drafts=[[11, 12, 13], [-1, -1, -1], [7, 8, 9]],
+        emit=[[21, 22, 23, 40], [50, -1, -1, -1], [60, -1, -1, -1]], n_emit=[4, 1, 1],
+        ctx=[100, 7, 0], N=N, mask_id=MASK)
+    M = MASK
+    assert tokens.tolist() == [[40, 11, 12, 13, M, M, M, M],   # FULL: [t, d1..d3, MASK x 4]
+                               [50, M, M, M, M, M, M, M],      # FRESH: [t, MASK x 7]
+                               [60, 7, 8, 9, M, M, M, M]]
+    assert pos.tolist() == [list(range(100, 108)), list(range(7, 15)), list(range(0, 8))]
+    assert is_mask.tolist() == [[False] * 4 + [True] * 4, [False] + [True] * 7, [False] * 4 + [True] * 4]
+    tokens, _, is_mask = accept.block_assemble([1, 0], [[5], [-1]], [[3, 4], [6, -1]], [2, 1], [9, 9], 2, MASK)
+    assert tokens.tolist() == [[4, 5, M, M], [6, M, M, M]]
+    # a step not taken (n_emit 0) or a state that is neither FULL nor FRESH
+    tokens, _, is_mask = accept.block_assemble([3, 1], [[1, 2, 3], [1, 2, 3]], [[-1] * 4, [5, -1, -1, -1]],
+                                               [0, 1], [4, 4], 4, MASK)
+    assert (tokens == -1).all() and not is_mask.any()
+
+
+@pytest.mark.parametrize("N", [2, 4])
+def test_block_assemble_feeds_the_cache_every_emitted_token_once(N):
+    """An oracle decoding loop in which each step's block comes from
+    block_assemble: the tokens the KV cache commits (rows 0..a of each block)
+    are exactly the emitted stream, in order, one token late, and row 0 of
+    every block sits at the position of that token in the stream. The
+    drafts of each block are the ones the next accept step verifies."""
+    V, C, steps, R = 6, 16, 40, 2 * N
+    rng = np.random.default_rng(5)
+    ctx0 = rng.integers(10, 50, C)
+    # clean rows: a fixed P per position; MASK rows: a nearby Q
+    P = rng.dirichlet(np.ones(V), size=(C, 200))
+    Q = 0.6 * P + 0.4 * rng.dirichlet(np.ones(V), size=(C, 200))
+    ctx = ctx0.copy()
+    n = np.zeros(C, int)
+    drafts = np.full((C, N - 1), -1)
+    q_row = np.zeros(C, int)
+    # step 0's block is the prompt's last token followed by MASK rows
+    first = rng.integers(0, V, C)
+    tokens = np.full((C, R), MASK)
+    tokens[:, 0] = first
+    is_mask = np.broadcast_to(np.arange(R)[None, :] > 0, (C, R))
+    prev = None
+    emitted = [[int(first[b])] for b in range(C)]  # the stream: prompt's last token, then emits
+    committed = [[] for _ in range(C)]
+    for step in range(steps):
+        for b in range(C):  # the block carries the drafts this step verifies
+            assert tokens[b, 1:1 + n[b]].tolist() == drafts[b, :n[b]].tolist()
+        pos = ctx[:, None] + np.arange(R)[None, :]
+        cur = np.empty((C, R, V))
+        for b in range(C):
+            for i in range(R):
+                src = Q if is_mask[b, i] else P
+                cur[b, i] = logits_of(src[b, pos[b, i] - ctx0[b] + 1])
+        u = philox.step_uniforms(17, step, C, N)
+        out = accept.accept_step(cur, prev, n, drafts, q_row, u, N)
+        for b in range(C):
+            committed[b] += tokens[b, : out["kv_commit"][b]].tolist()
+            emitted[b] += out["emit"][b, : out["n_emit"][b]].tolist()
+        ctx = ctx + out["kv_commit"]
+        n, drafts, q_row, prev = out["n_draft_next"], out["drafts_next"], out["q_row_next"], cur
+        tokens, positions, is_mask = accept.block_assemble(n, drafts, out["emit"], out["n_emit"], ctx, N, MASK)
+        for b in range(C):
+            # row 0 is the newest emitted token, at its index in the stream
+            assert tokens[b, 0] == emitted[b][-1]
+            assert positions[b, 0] == ctx0[b] + len(emitted[b]) - 1
+        assert (is_mask.sum(1) == np.where(n == N - 1, N, 2 * N - 1)).all()
+    for b in range(C):
+        assert committed[b] == emitted[b][:-1]

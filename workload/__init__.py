@@ -140,3 +140,25 @@ def lora_case(seed, M, K, Nout, r, dtype=torch.bfloat16, device="cpu",
 def stride_mask(M, N):
     """MASK rows of a batch of 2N-row stride blocks: rows N..2N-1 of each."""
     return (np.arange(M) % (2 * N)) >= N
+
+
+def step_outputs(seed, C, N, V, bad_frac=0.0):
+    """Synthetic per-sequence state and step outputs (int32 numpy arrays),
+    shaped like what one accept step leaves behind: n_draft in {0, N-1},
+    drafts, emit with n_emit valid entries (-1 after), ctx after the commit.
+    A fraction bad_frac of the sequences gets an invalid n_draft or
+    n_emit."""
+    rng = np.random.default_rng(seed_of(seed, "step-outputs"))
+    n_draft = np.where(rng.random(C) < 0.7, N - 1, 0).astype(np.int32)
+    drafts = rng.integers(0, V, (C, N - 1)).astype(np.int32)
+    drafts[n_draft == 0] = -1
+    n_emit = rng.integers(1, N + 1, C).astype(np.int32)
+    emit = rng.integers(0, V, (C, N)).astype(np.int32)
+    emit[np.arange(N)[None, :] >= n_emit[:, None]] = -1
+    ctx = rng.integers(0, 32768, C).astype(np.int32)
+    bad = rng.random(C) < bad_frac
+    kind = rng.integers(0, 3, C)
+    n_draft[bad & (kind == 0)] = 1 if N > 2 else -1   # neither FULL nor FRESH
+    n_emit[bad & (kind == 1)] = 0                     # step not taken
+    n_emit[bad & (kind == 2)] = N + 1
+    return n_draft, drafts, emit, n_emit, ctx
