@@ -99,7 +99,8 @@ struct GemmParams {
   const uint16_t* w;    // [Nout][K]
   float* y;             // [splits][M][Nout]
   // gated epilogue (R16 > 0): MASK rows get y = acc + scale * U B^T
-  const float* u;       // [M][r] fp32 U = x A^T
+  const float* u;       // U = x A^T as u_splits split-K partials [u_splits][M][r] fp32
+  int u_splits;         // summed in split order while staged into LDS
   const uint16_t* b;    // [Nout][r]
   const uint8_t* mask;  // [M]
   float scale;
@@ -282,10 +283,21 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   if constexpr (R16 > 0) {
     constexpr int r4 = 4 * R16;  // float4 per U row
     stage_barrier();             // every wave is done with the stages
+    const long pstride = static_cast<long>(p.M) * 16 * R16;  // elements between split partials
     for (int e = tid; e < BM * r4; e += 256) {
       const int row = e / r4, q = e % r4;
       const float* src = p.u + static_cast<long>(min(m_blk + row, p.M - 1)) * 16 * R16 + 4 * q;
-      *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = *reinterpret_cast<const f32x4*>(src);
+      f32x4 part[kMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)  // all loads first; missing splits re-read split 0, unused
+        part[sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
+      f32x4 v = part[0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplits; ++sp)
+        if (sp < p.u_splits)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
+      *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = v;
     }
     wait_vm_lgkm0<0>();
     stage_barrier();
@@ -554,12 +566,15 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
-  if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
+  // U's split-K partials; the GEMM sums them (in split order, as the
+  // reduction kernel of gated_lora_apply does) when it stages its U rows
+  if (launch_lora_u_partials(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
   p.y = y;
-  p.u = lora_u_of(ws, M, r);
+  p.u = static_cast<const float*>(ws);
+  p.u_splits = u_splits(K);
   p.b = static_cast<const uint16_t*>(B);
   p.mask = is_mask;
   p.scale = scale;
