@@ -87,11 +87,20 @@ struct AttnOps<uint16_t> {
     return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
   }
   static __device__ __forceinline__ bf16x8 zero() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
+  // Loads are unconditional (callers pass pointers that are always inside
+  // the buffers: a masked lane or an invalid page reads page 0 or row 0) and
+  // a select drops the value: a load under a branch makes the compiler wait
+  // for every load in flight at the join, once per load.
+  static __device__ __forceinline__ bf16x8 keep(bf16x8 v, bool valid) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    const uint32_t m = valid ? ~0u : 0u;
+    return __builtin_bit_cast(bf16x8, u32x4{w[0] & m, w[1] & m, w[2] & m, w[3] & m});
+  }
 
   template <int D>
   static __device__ __forceinline__ void load_q(Regs<D>& r, const uint16_t* qrow, bool valid, int hh) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) r.q[s] = valid ? load16(qrow + 16 * s + 8 * hh) : zero();
+    for (int s = 0; s < D / 16; ++s) r.q[s] = keep(load16(qrow + 16 * s + 8 * hh), valid);
   }
   // K operand: lane (row i, half hh) at k-step s holds dims 16s + 8hh .. +8
   // of tile key pi(i).
@@ -99,7 +108,7 @@ struct AttnOps<uint16_t> {
   static __device__ __forceinline__ void load_k(Regs<D>& r, const uint16_t* kpage, bool valid, int slot, int hh) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      r.k[s] = valid ? load16_stream(kpage + ((2 * s + hh) * 16 + slot) * 8) : zero();
+      r.k[s] = keep(load16_stream(kpage + ((2 * s + hh) * 16 + slot) * 8), valid);
   }
   // V^T operand: lane (dim d, half hh) at k-step p (= tile page p) holds
   // slots 8hh .. 8hh+7 of dim d, which the page stores as 16 contiguous
@@ -110,15 +119,15 @@ struct AttnOps<uint16_t> {
                                                 int hh, int first_key, int limit) {
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) {
-      bf16x8 v = valid ? load16_stream(vpage + (hh * D + nb * 32 + lane32) * 8) : zero();
-      if (first_key + 8 > limit) {
-        u32x4 w = __builtin_bit_cast(u32x4, v);
+      const bf16x8 v = keep(load16_stream(vpage + (hh * D + nb * 32 + lane32) * 8), valid);
+      // keys at or past limit are cleared without a branch (a branch on the
+      // loaded value would make the compiler wait for it right here)
+      const int nkeep = limit - first_key;  // keys of this lane's 8 that stay
+      u32x4 w = __builtin_bit_cast(u32x4, v);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (first_key + k >= limit) w[k >> 1] &= (k & 1) ? 0x0000ffffu : 0xffff0000u;
-        v = __builtin_bit_cast(bf16x8, w);
-      }
-      r.v[nb][p] = v;
+      for (int k = 0; k < 4; ++k)
+        w[k] &= (2 * k < nkeep ? 0x0000ffffu : 0u) | (2 * k + 1 < nkeep ? 0xffff0000u : 0u);
+      r.v[nb][p] = __builtin_bit_cast(bf16x8, w);
     }
   }
   template <int D>
@@ -161,6 +170,10 @@ struct AttnOps<uint16_t> {
 template <>
 struct AttnOps<float> {
   static constexpr int kKStep = 2;
+  // as in the bf16 case: unconditional load, then the value is dropped
+  static __device__ __forceinline__ float keep(float v, bool valid) {
+    return __uint_as_float(__float_as_uint(v) & (valid ? ~0u : 0u));
+  }
   template <int D>
   struct Regs {
     float q[D / 2];
@@ -170,14 +183,14 @@ struct AttnOps<float> {
   template <int D>
   static __device__ __forceinline__ void load_q(Regs<D>& r, const float* qrow, bool valid, int hh) {
 #pragma unroll
-    for (int s = 0; s < D / 2; ++s) r.q[s] = valid ? qrow[2 * s + hh] : 0.f;
+    for (int s = 0; s < D / 2; ++s) r.q[s] = keep(qrow[2 * s + hh], valid);
   }
   template <int D>
   static __device__ __forceinline__ void load_k(Regs<D>& r, const float* kpage, bool valid, int slot, int hh) {
 #pragma unroll
     for (int s = 0; s < D / 2; ++s) {
       int d = 2 * s + hh;
-      r.k[s] = valid ? kpage[((d >> 2) * 16 + slot) * 4 + (d & 3)] : 0.f;
+      r.k[s] = keep(kpage[((d >> 2) * 16 + slot) * 4 + (d & 3)], valid);
     }
   }
   // V^T operand for k-step e of page p: key 16p + 8hh + e%8.
@@ -189,7 +202,7 @@ struct AttnOps<float> {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         bool ok = valid && (first_key + k < limit);
-        r.v[nb][8 * p + k] = ok ? vpage[(hh * D + nb * 32 + lane32) * 8 + k] : 0.f;
+        r.v[nb][8 * p + k] = keep(vpage[(hh * D + nb * 32 + lane32) * 8 + k], ok);
       }
   }
   template <int D>
