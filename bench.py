@@ -310,6 +310,9 @@ def main():
                          "with S workgroups per KV-head group")
     ap.add_argument("--proposal", choices=("sample", "argmax"), default="sample",
                     help="draft proposals: sampled from q (default) or argmax q")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (two graphs: even and odd steps); every "
+                         f"{PROBE_EVERY}th timed step runs eagerly with the event probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -384,7 +387,39 @@ def main():
     proj_ev = [[(ev(), ev(), ev()) for _ in range(L)] for _ in probes]
     acc_ev = [(ev(), ev()) for _ in probes]
 
+    # --graph: the whole step on one side stream, the logits of step t copied
+    # by the device (index from a step word in HBM) into one of two fixed
+    # buffers, the accept reading its Philox step from that word; captured
+    # once per parity and replayed.
+    gs = torch.cuda.Stream() if args.graph else None
+    if args.graph:
+        all_lg = torch.stack(logits)
+        del logits[:]
+        buf = [torch.empty_like(all_lg[0]) for _ in range(2)]
+        step_t = torch.zeros(1, dtype=torch.int64, device=dev)
+        with torch.cuda.stream(gs):
+            layer_calls = []
+            for l in range(L):
+                lay, kv = st["layers"][l], st["kvs"][l]
+                p = lay["proj"]
+                lg = lambda name, x: dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"],
+                                                              st["mask"], p[name]["y"], st["lora_ws"])
+                layer_calls.append(dict(
+                    qkv=[lg("qkv", lay["x"])],
+                    kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
+                    att=dvd.prepare_attention(kv, lay["q"], ctx, max_len, lay["out"], ws=att_ws,
+                                              slices=args.slices, dev_err=err),
+                    o=lg("o", lay["xo"])))
+
     def step(t, timed_idx=None):
+        if args.graph:
+            par = t % 2
+            with torch.cuda.stream(gs):
+                if timed_idx is None:
+                    graphs[par].replay()
+                else:
+                    graph_body(par, timed_idx)
+            return
         for l in range(L):
             c = layer_calls[l]
             if timed_idx is not None:
@@ -409,6 +444,44 @@ def main():
                        ws=acc_ws, ctx=ctx, dev_err=err, proposal=cfg["proposal"])
         if timed_idx is not None:
             acc_ev[timed_idx][1].record()
+
+    def graph_body(par, timed_idx=None):
+        torch.index_select(all_lg, 0, step_t, out=buf[par].unsqueeze(0))
+        for l in range(L):
+            c = layer_calls[l]
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][0].record()
+            for f in c["qkv"]:
+                f()
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][1].record()
+            c["kvw"]()
+            if timed_idx is not None:
+                att_ev[timed_idx][l][0].record()
+            c["att"]()
+            if timed_idx is not None:
+                att_ev[timed_idx][l][1].record()
+            c["o"]()
+            if timed_idx is not None:
+                proj_ev[timed_idx][l][2].record()
+        s_in, s_out = (s_a, s_b) if par == 0 else (s_b, s_a)
+        if timed_idx is not None:
+            acc_ev[timed_idx][0].record()
+        dvd.isd_accept(buf[par], buf[1 - par], s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws, ctx=ctx,
+                       dev_err=err, proposal=cfg["proposal"], step_dev=step_t, stream=gs)
+        if timed_idx is not None:
+            acc_ev[timed_idx][1].record()
+        step_t.add_(1)
+
+    if args.graph:
+        graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+        torch.cuda.synchronize()
+        for par in (0, 1):
+            with torch.cuda.graph(graphs[par], stream=gs):
+                graph_body(par)
+        torch.cuda.synchronize()
+        assert int(step_t.item()) == 0  # capture records, it does not run
+        log("[bench] step captured as two HIP graphs")
 
     for t in range(W):
         step(t)
@@ -465,6 +538,8 @@ def main():
             "proposal": cfg["proposal"],
             "attention_split": ("batch-invariant, chunks of %d tiles" % -args.slices if args.slices < 0
                                 else "stream-K, %s slices" % (args.slices or "automatic")),
+            "launch": ("HIP graph replay per step (every %dth timed step eager, with the event probes)" % PROBE_EVERY
+                       if args.graph else "eager"),
         },
         "roofline": {
             "kernel": "isd_attention (main + LSE merge launches of one call)",

@@ -69,6 +69,7 @@ class IsdAcceptArgs(ctypes.Structure):
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("dev_err", ctypes.c_void_p),
         ("proposal", ctypes.c_int32),
+        ("step_dev", ctypes.c_void_p),
     ]
 
 
@@ -249,11 +250,13 @@ class AcceptOutputs:
 
 
 def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
-               diag=False, dev_err=None, ctx=None, stream=None, proposal="sample"):
+               diag=False, dev_err=None, ctx=None, stream=None, proposal="sample", step_dev=None):
     """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
     AcceptOutputs (device tensors) and writes state_out. If ctx (int32 [C])
     is given, the kernel adds kv_commit to it. proposal: "sample" or
-    "argmax" (drafts = argmax of the MASK rows)."""
+    "argmax" (drafts = argmax of the MASK rows). step_dev: optional int64
+    device tensor [1] holding the step number (then `step` is ignored), for
+    calls captured in a graph."""
     C, rows, ld = logits.shape
     V = ld if V is None else V
     if out is None:
@@ -280,6 +283,7 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     args.ws_bytes = ws.numel() * ws.element_size()
     args.dev_err = None if dev_err is None else dev_err.data_ptr()
     args.proposal = PROPOSE[proposal]
+    args.step_dev = None if step_dev is None else step_dev.data_ptr()
     _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
     return out
 

@@ -42,6 +42,7 @@ struct AcceptParams {
   int C, N, V, rows, nch, ns;
   isd_seq_state in, out;
   uint64_t seed, step;
+  const uint64_t* step_dev;  // when set, the step number comes from here
   int32_t *accepted, *n_emit, *emit, *kv_commit, *ctx;
   float *p_x, *resid_mass, *row_m, *row_s;
   float2* stats;    // [C][rows][nch] (chunk max, chunk sum)
@@ -293,8 +294,10 @@ __device__ void decide(const AcceptParams& p, int b, Decision& d) {
   }
   for (int i = tid; i < R * p.nch; i += kThreads)
     d.st[i / p.nch][i % p.nch] = p.stats[(static_cast<long>(b) * p.rows + i / p.nch) * p.nch + i % p.nch];
-  if (tid < 2 * N)
-    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), p.step, 0ull, p.seed, 0ull));
+  if (tid < 2 * N) {
+    const uint64_t step = p.step_dev ? *p.step_dev : p.step;
+    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), step, 0ull, p.seed, 0ull));
+  }
   __syncthreads();
   // every thread clamps n the same way; thread 0 records what was wrong
   const int n_raw = s_n;
@@ -778,6 +781,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.out = a->out;
   p.seed = a->seed;
   p.step = a->step;
+  p.step_dev = a->step_dev;
   p.accepted = a->accepted;
   p.n_emit = a->n_emit;
   p.emit = a->emit;

@@ -227,6 +227,10 @@ typedef struct isd_accept_args {
   int32_t* dev_err;
   int32_t proposal;   /* ISD_PROPOSE_SAMPLE or ISD_PROPOSE_ARGMAX; the same on
                          consecutive steps of a sequence */
+  const uint64_t* step_dev; /* optional: when not NULL the step number is read
+                         from this device word and `step` is ignored, so one
+                         captured HIP graph can be replayed step after step
+                         (the caller advances the word between replays) */
 } isd_accept_args;
 
 size_t isd_accept_workspace_size(int C, int N, int V, int rows);

@@ -158,3 +158,34 @@ def test_block_assemble_rejects_bad_arguments_on_host(lib):
     assert f(ctypes.byref(st), 16, 16, 16, 4, 4, 7, None, 16, 16, None, None) == -1  # no tokens
     assert f(ctypes.byref(st), None, 16, 16, 4, 4, 7, 16, 16, 16, None, None) == -1  # no emit
     assert f(ctypes.byref(st), 16, 16, None, 4, 4, 7, 16, 16, 16, None, None) == -1  # positions need ctx
+
+
+def test_ctypes_structs_match_the_header_layout(tmp_path):
+    """The binding's ctypes structs have the sizes and field offsets the C
+    compiler gives the structs of include/isd.h."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no host C compiler")
+    structs = {"isd_accept_args": dvd.IsdAcceptArgs, "isd_seq_state": dvd.IsdSeqState,
+               "isd_kv_cache": dvd.IsdKvCache}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "isd.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            cf = "in" if fname == "in_" else fname
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {cf}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)

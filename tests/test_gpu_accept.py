@@ -441,3 +441,70 @@ def test_block_assemble_matches_oracle(N):
                                               None, N, mask_id, is_mask=None)
     torch.cuda.synchronize()
     assert pos2 is None and np.array_equal(tok2.cpu().numpy(), o_tok)
+
+
+def test_graph_replay_of_the_device_step_matches_eager():
+    """The device side of a decode step (accept with the step number read
+    from device memory, block assembly, step advance) captured as two HIP
+    graphs (even and odd steps swap the state and logits buffers) and
+    replayed for 12 steps gives the same bits as the same calls run eagerly
+    with explicit step numbers. Eager work (the next logits) and host
+    synchronisations run between the replays; every replay is checked."""
+    C, N, V, seed, steps = 64, 4, 4096, 31, 12
+    R, mask_id = 2 * N, V
+    print(f"graph replay C={C} N={N} V={V}", flush=True)
+    teacher = workload.TeacherLogits(seed, C, V, steps * N + R + 1, 3.0, 0.5, torch.bfloat16, DEV)
+    ctx0 = torch.from_numpy(workload.contexts(seed, C, ("uniform", 10, 500)).astype(np.int64)).to(DEV)
+    s = torch.cuda.Stream()
+
+    def side():
+        st = [dvd.SeqState(C, N), dvd.SeqState(C, N)]
+        return dict(st=st, ctx=ctx0.to(torch.int32).clone(), out=dvd.AcceptOutputs(C, N, R, DEV, diag=False),
+                    ws=torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=DEV),
+                    err=torch.zeros(1, dtype=torch.int32, device=DEV),
+                    tok=torch.empty((C, R), dtype=torch.int32, device=DEV),
+                    pos=torch.empty((C, R), dtype=torch.int32, device=DEV),
+                    msk=torch.empty((C, R), dtype=torch.uint8, device=DEV))
+
+    e, gs = side(), side()
+    buf = [torch.empty((C, R, V), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    step_t = torch.zeros(1, dtype=torch.int64, device=DEV)
+
+    def device_step(x, par, lg, prev, step, step_dev, stream):
+        dvd.isd_accept(lg, prev, x["st"][par], x["st"][1 - par], N, seed, step, out=x["out"], ws=x["ws"],
+                       ctx=x["ctx"], dev_err=x["err"], stream=stream, step_dev=step_dev)
+        dvd.isd_block_assemble(x["st"][1 - par], x["out"].emit, x["out"].n_emit, x["ctx"], N, mask_id,
+                               tokens=x["tok"], positions=x["pos"], is_mask=x["msk"], dev_err=x["err"], stream=stream)
+
+    graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+    torch.cuda.synchronize()
+    for par in (0, 1):
+        with torch.cuda.graph(graphs[par], stream=s):
+            device_step(gs, par, buf[par], buf[1 - par], 0, step_t, s)
+            step_t.add_(1)
+    torch.cuda.synchronize()
+    # capturing launched nothing: reset what the capture may have touched
+    step_t.zero_()
+
+    prev_e = None
+    for t in range(steps):
+        par = t % 2
+        lg = teacher.block(t, e["ctx"].long(), ctx0, e["st"][par].n_draft.long(), R).contiguous()
+        with torch.cuda.stream(s):
+            buf[par].copy_(lg)
+            graphs[par].replay()
+        device_step(e, par, lg, prev_e, t, None, torch.cuda.current_stream())
+        prev_e = lg
+        torch.cuda.synchronize()
+        assert e["err"].item() == 0 and gs["err"].item() == 0
+        assert step_t.item() == t + 1
+        for k in ("accepted", "n_emit", "emit", "kv_commit"):
+            assert torch.equal(getattr(e["out"], k), getattr(gs["out"], k)), (t, k)
+        for k in ("n_draft", "drafts", "q_x", "q_m", "q_s", "q_row"):
+            a, b = getattr(e["st"][1 - par], k), getattr(gs["st"][1 - par], k)
+            assert torch.equal(a.view(torch.int32) if a.is_floating_point() else a,
+                               b.view(torch.int32) if b.is_floating_point() else b), (t, k)
+        for k in ("ctx", "tok", "pos", "msk"):
+            assert torch.equal(e[k], gs[k]), (t, k)
+    # the trajectory moved: FULL steps happened and tokens were emitted
+    assert int(e["ctx"].sum() - ctx0.sum()) > C * steps
