@@ -67,14 +67,15 @@ def accept_bytes(n_draft, accepted, cfg):
 
 
 def projection_flops(cfg):
-    """Algorithmic flops of the two gated projections of one layer: the base
-    product over all 2N*C rows plus the rank-r delta (x A^T then U B^T) on the
-    N*C MASK rows."""
+    """Algorithmic flops of the two projections of one layer: the base
+    product over all 2N*C rows plus, when the LoRA is on, the rank-r delta
+    (x A^T then U B^T) on the N*C MASK rows."""
     C, N, H, r = cfg["C"], cfg["N"], cfg["hidden"], cfg["lora_rank"]
     M, Mm = C * 2 * N, C * N
     n_qkv = (cfg["Hq"] + 2 * cfg["Hkv"]) * cfg["D"]
-    qkv = 2 * M * H * n_qkv + 3 * 2 * Mm * r * (H + n_qkv // 3)
-    o = 2 * M * H * H + 2 * Mm * r * (H + H)
+    lora = cfg.get("lora", "gated") == "gated"
+    qkv = 2 * M * H * n_qkv + lora * 3 * 2 * Mm * r * (H + n_qkv // 3)
+    o = 2 * M * H * H + lora * 2 * Mm * r * (H + H)
     return qkv, o
 
 
@@ -310,6 +311,9 @@ def main():
                          "with S workgroups per KV-head group")
     ap.add_argument("--proposal", choices=("sample", "argmax"), default="sample",
                     help="draft proposals: sampled from q (default) or argmax q")
+    ap.add_argument("--lora", choices=("gated", "off"), default="gated",
+                    help="projections with the gated LoRA of R-ISD (default) or the base GEMM alone "
+                         "(the ratio of the two step times is the LoRA overhead alpha)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (two graphs: even and odd steps); every "
                          f"{PROBE_EVERY}th timed step runs eagerly with the event probes")
@@ -338,7 +342,7 @@ def main():
 
     import draft_verify_decoding_amd as dvd
 
-    cfg = dict(CFG, proposal=args.proposal)
+    cfg = dict(CFG, proposal=args.proposal, lora=args.lora)
     dev = "cuda"
     torch.cuda.set_device(0)
     dvd.lib()
@@ -365,8 +369,9 @@ def main():
     for l in range(L):
         lay, kv = st["layers"][l], st["kvs"][l]
         p = lay["proj"]
-        lg = lambda name, x: dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"], st["mask"],
-                                                      p[name]["y"], st["lora_ws"])
+        lg = lambda name, x: (dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"], st["mask"],
+                                                       p[name]["y"], st["lora_ws"]) if args.lora == "gated"
+                              else dvd.prepare_linear(x, p[name]["W"], p[name]["y"]))
         layer_calls.append(dict(
             qkv=[lg("qkv", lay["x"])],
             kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
@@ -402,8 +407,9 @@ def main():
             for l in range(L):
                 lay, kv = st["layers"][l], st["kvs"][l]
                 p = lay["proj"]
-                lg = lambda name, x: dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"],
-                                                              st["mask"], p[name]["y"], st["lora_ws"])
+                lg = lambda name, x: (dvd.prepare_linear_gated(x, p[name]["W"], p[name]["A"], p[name]["B"],
+                                                               st["mask"], p[name]["y"], st["lora_ws"])
+                                      if args.lora == "gated" else dvd.prepare_linear(x, p[name]["W"], p[name]["y"]))
                 layer_calls.append(dict(
                     qkv=[lg("qkv", lay["x"])],
                     kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
@@ -532,12 +538,15 @@ def main():
         "config": {
             "workload": "stationary batch C=64, N=4 (8-row blocks), 8B-class GQA 32/8 heads, head_dim 128, "
                         "36 layers, bf16 paged KV (16-token pages), contexts U{1024..8192}, vocab 151936, "
-                        "acceptance ~0.9, gated-LoRA rank-32 Q/K/V/O projections; MLP and LM head not included",
+                        "acceptance ~0.9, " + ("gated-LoRA rank-32" if args.lora == "gated" else "base (no LoRA)")
+                        + " Q/K/V/O projections; MLP and LM head not included",
             "C": C, "N": N, "layers": L, "Hq": Hq, "Hkv": cfg["Hkv"], "head_dim": D, "vocab": V,
             "global_batch": C, "seq_len": int(np.mean(ctxs[W])), "parallelism": "none (1 GPU)",
             "proposal": cfg["proposal"],
             "attention_split": ("batch-invariant, chunks of %d tiles" % -args.slices if args.slices < 0
                                 else "stream-K, %s slices" % (args.slices or "automatic")),
+            "projections": ("gated LoRA rank %d on MASK rows" % cfg["lora_rank"] if args.lora == "gated"
+                            else "base GEMM only (no LoRA)"),
             "launch": ("HIP graph replay per step (every %dth timed step eager, with the event probes)" % PROBE_EVERY
                        if args.graph else "eager"),
         },
@@ -561,8 +570,8 @@ def main():
         "mean_accepted": round(float(accs[W:].mean()), 4),
     }
     qkv_flops, o_flops = projection_flops(cfg)
-    res["projection_us_per_launch"] = {"qkv_gated": round(float(qkv_ms.mean()) * 1e3, 2),
-                                       "o_gated": round(float(o_ms.mean()) * 1e3, 2)}
+    res["projection_us_per_launch"] = {"qkv": round(float(qkv_ms.mean()) * 1e3, 2),
+                                       "o": round(float(o_ms.mean()) * 1e3, 2)}
     proj_tflops = (qkv_flops + o_flops) * len(probes) * L / ((np.sum(qkv_ms) + np.sum(o_ms)) / 1e3) / 1e12
     res["projection_mfma"] = {"achieved": round(float(proj_tflops), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(float(proj_tflops) / MFMA_BF16_PEAK_TFLOPS, 4)}

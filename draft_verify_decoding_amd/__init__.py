@@ -381,6 +381,11 @@ def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, d
                     keep=(s, kv, q, ctx, out, ws, dev_err))
 
 
+def prepare_linear(x, W, y, stream=None):
+    M, K = x.shape
+    return Prepared("isd_linear", _p(x), _p(W), M, K, W.shape[0], _p(y), _stream(stream), keep=(x, W, y))
+
+
 def prepare_linear_gated(x, W, A, B, is_mask, y, ws, scale=1.0, stream=None):
     M, K = x.shape
     return Prepared("isd_linear_gated", _p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, W.shape[0], A.shape[0],

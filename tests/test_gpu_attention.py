@@ -241,3 +241,27 @@ def test_invariant_split_flags_sequences_beyond_max_len():
     kp, vp = oracle_pages(case)
     want = ref.block_attention(to64(case.q[:2]), kp, vp, case.table[:2], case.ctx[:2])
     assert slab_errors(got[:2], want).max() < 2e-3
+
+
+def test_invariant_split_at_the_bench_shape_sampled_rows():
+    """The stationary-batch shape (C=64, 8-row blocks, 32/8 heads, ragged
+    1K-8K contexts) in the batch-invariant split with 64-tile chunks: every
+    row of a sample of 16 sequences equals, bit for bit, its one-row call
+    with ctx + i cached tokens made as a separate batch."""
+    C, rows, t = 64, 8, 64
+    case = workload.AttentionCase(3, C=C, rows=rows, Hq=32, Hkv=8, D=128, ctx=("uniform", 1024, 8192))
+    print(f"invariant split at C={C}", flush=True)
+    kv, err = fill_cache(case)
+    max_len = int(case.lengths.max())
+    ctx_d = torch.from_numpy(case.ctx).to(DEV)
+    q = case.q.to(DEV)
+    blk = dvd.isd_attention(kv, q, ctx_d, max_len=max_len, slices=dvd.attn_invariant(t), dev_err=err)
+    seqs = torch.from_numpy(np.random.default_rng(9).choice(C, 16, replace=False)).to(DEV)
+    ar = copy.copy(kv)
+    ar.block_table = kv.block_table[seqs].repeat_interleave(rows, dim=0).contiguous()
+    ctx1 = (ctx_d[seqs][:, None] + torch.arange(rows, device=DEV, dtype=torch.int32)[None, :]).reshape(-1).contiguous()
+    q1 = q[seqs].reshape(16 * rows, 1, 32, 128).contiguous()
+    one = dvd.isd_attention(ar, q1, ctx1, max_len=max_len, slices=dvd.attn_invariant(t), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(blk[seqs]), bits(one))
