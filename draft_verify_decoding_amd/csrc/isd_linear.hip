@@ -71,21 +71,32 @@ __device__ __forceinline__ UFrag<R16> u_frag(const float* row, int hh) {
   return uf;
 }
 
-// U B^T for columns n0.. of B (bf16 [Nout][r]); columns past Nout give 0.
+// The B^T operand of the delta for columns n0.. of B (bf16 [Nout][r]):
+// lane (j, hh) holds B[n0 + j][16k + 8hh .. +8] for every 16-deep step k;
+// columns past Nout give 0.
 template <int R16>
-__device__ __forceinline__ f32x16 lora_delta(const UFrag<R16>& uf, const uint16_t* B, int Nout, int n0, int lane32,
-                                             int hh) {
+struct BFrag {
+  u32x4 v[R16];
+};
+template <int R16>
+__device__ __forceinline__ BFrag<R16> b_frag(const uint16_t* B, int Nout, int n0, int lane32, int hh) {
   constexpr int r = 16 * R16;
   const int bcol = n0 + lane32;
-  u32x4 bv[R16];
+  BFrag<R16> bf;
 #pragma unroll
   for (int k = 0; k < R16; ++k)
-    bv[k] = bcol < Nout ? *reinterpret_cast<const u32x4*>(B + static_cast<long>(bcol) * r + 16 * k + 8 * hh)
-                        : u32x4{0, 0, 0, 0};
+    bf.v[k] = bcol < Nout ? *reinterpret_cast<const u32x4*>(B + static_cast<long>(bcol) * r + 16 * k + 8 * hh)
+                          : u32x4{0, 0, 0, 0};
+  return bf;
+}
+
+// U B^T of one 32x32 block from its fragments.
+template <int R16>
+__device__ __forceinline__ f32x16 lora_delta(const UFrag<R16>& uf, const BFrag<R16>& bf) {
   f32x16 dh = {}, dl = {};
 #pragma unroll
   for (int k = 0; k < R16; ++k) {
-    const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[k]);
+    const bf16x8 bb = __builtin_bit_cast(bf16x8, bf.v[k]);
     dh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf.hi[k], bb, dh, 0, 0, 0);
     dl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf.lo[k], bb, dl, 0, 0, 0);
   }
@@ -246,8 +257,49 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   const int nk_all = p.K / kBK;
   const int kb = split * nk_all / p.splits, nk = (split + 1) * nk_all / p.splits - kb;
   constexpr int kLoads = A_LOADS + B_LOADS;
+
+  // Gated: the U partials of the workgroup's rows and the B fragments of the
+  // wave's column blocks are fetched ahead of the K loop, so the epilogue
+  // waits on no memory. Thread t owns float4 t, t + 256, ... of the BM x r
+  // U block; the partials are summed in split order (the order of the
+  // stand-alone reduction kernel).
+  // (Tiles whose U block and B fragments would not fit the register file,
+  // 128-row tiles and the widest ranks, fetch them in the epilogue instead.)
+  constexpr int kR16 = R16 > 0 ? R16 : 1;
+  constexpr int r4 = 4 * kR16;  // float4 per U row
+  constexpr int kUPer = (BM * r4) / 256;
+  static_assert(R16 == 0 || (BM * r4) % 256 == 0, "U block split evenly over the threads");
+  constexpr bool kPrefetch = R16 > 0 && TM == 1 && TN * R16 <= 18;
+  f32x4 upart[kPrefetch ? kUPer : 1][kPrefetch ? kMaxSplits : 1];
+  BFrag<kR16> bfr[kPrefetch ? TN : 1];
+  if constexpr (kPrefetch) {
+    const long pstride = static_cast<long>(p.M) * 16 * R16;  // elements between split partials
+#pragma unroll
+    for (int i = 0; i < kUPer; ++i) {
+      const int e = tid + 256 * i, row = e / r4, q = e % r4;
+      const float* src = p.u + static_cast<long>(min(m_blk + row, p.M - 1)) * 16 * R16 + 4 * q;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)  // missing splits re-read split 0, unused
+        upart[i][sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = b_frag<R16>(p.b, p.Nout, n_blk + wn + 32 * j, lane32, hh);
+  }
 #pragma unroll
   for (int d = 0; d < STAGES - 1; ++d) load_slab((kb + min(d, nk - 1)) * kBK, d);
+  f32x4 usum[kPrefetch ? kUPer : 1];
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int i = 0; i < kUPer; ++i) {
+      f32x4 v = upart[i][0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplits; ++sp)
+        if (sp < p.u_splits)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = v[c] + upart[i][sp][c];
+      usum[i] = v;
+    }
+  }
   // unrolled over kUnroll slabs: the compiler proves that reading one stage
   // need not wait for the loads into the others only inside one trip of the
   // loop, and waits for every load once per trip
@@ -271,7 +323,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   }
   wait_vm_lgkm0<0>();
 
-  // Gated: the workgroup copies the U rows of its BM rows into LDS, reusing
+  // Gated: the workgroup writes the U rows of its BM rows into LDS, reusing
   // the stages (rows padded by 4 floats so the fragment reads spread over the
   // banks); each wave then splits its rows once for all of its column blocks.
   constexpr int kUStride = 16 * R16 + 4;
@@ -281,23 +333,30 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     return reinterpret_cast<float*>(stage_ptr(row / kURowsPerStage)) + (row % kURowsPerStage) * kUStride;
   };
   if constexpr (R16 > 0) {
-    constexpr int r4 = 4 * R16;  // float4 per U row
-    stage_barrier();             // every wave is done with the stages
-    const long pstride = static_cast<long>(p.M) * 16 * R16;  // elements between split partials
-    for (int e = tid; e < BM * r4; e += 256) {
-      const int row = e / r4, q = e % r4;
-      const float* src = p.u + static_cast<long>(min(m_blk + row, p.M - 1)) * 16 * R16 + 4 * q;
-      f32x4 part[kMaxSplits];
+    stage_barrier();  // every wave is done with the stages
+    if constexpr (kPrefetch) {
 #pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)  // all loads first; missing splits re-read split 0, unused
-        part[sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
-      f32x4 v = part[0];
+      for (int i = 0; i < kUPer; ++i) {
+        const int e = tid + 256 * i, row = e / r4, q = e % r4;
+        *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = usum[i];
+      }
+    } else {
+      const long pstride = static_cast<long>(p.M) * 16 * R16;
+      for (int e = tid; e < BM * r4; e += 256) {
+        const int row = e / r4, q = e % r4;
+        const float* src = p.u + static_cast<long>(min(m_blk + row, p.M - 1)) * 16 * R16 + 4 * q;
+        f32x4 part[kMaxSplits];
 #pragma unroll
-      for (int sp = 1; sp < kMaxSplits; ++sp)
-        if (sp < p.u_splits)
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+          part[sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
+        f32x4 v = part[0];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
-      *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = v;
+        for (int sp = 1; sp < kMaxSplits; ++sp)
+          if (sp < p.u_splits)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
+        *reinterpret_cast<f32x4*>(urow(row) + 4 * q) = v;
+      }
     }
     wait_vm_lgkm0<0>();
     stage_barrier();
@@ -324,7 +383,10 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
       const int col = n0 + lane32;
       f32x16 dl = {};
       if constexpr (R16 > 0) {
-        if (__any(live)) dl = lora_delta<R16>(uf, p.b, p.Nout, n0, lane32, hh);
+        if (__any(live)) {
+          if constexpr (kPrefetch) dl = lora_delta<R16>(uf, bfr[j]);
+          else dl = lora_delta<R16>(uf, b_frag<R16>(p.b, p.Nout, n0, lane32, hh));
+        }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -370,7 +432,7 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
     yv[e] = ((live >> e) & 1) ? p.y[static_cast<long>(row) * p.Nout + bcol] : 0.f;
   }
   const UFrag<R16> uf = u_frag<R16>(m0 + lane32 < p.M ? p.u + static_cast<long>(m0 + lane32) * 16 * R16 : nullptr, hh);
-  const f32x16 dl = lora_delta<R16>(uf, p.b, p.Nout, n0, lane32, hh);
+  const f32x16 dl = lora_delta<R16>(uf, b_frag<R16>(p.b, p.Nout, n0, lane32, hh));
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if ((live >> e) & 1) {
