@@ -261,7 +261,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   // Tile offsets of the sequences (prefix sum, stream-K split only).
   __shared__ int s_off[kMaxSeqs + 1];
-  __shared__ int s_part[512];
+  __shared__ int s_part[512 / kWave];  // per-wave totals of the prefix sum
   __shared__ int s_pid[2 * kTileBatch];  // page ids of the current tile batch
   int t_begin = 0, t_end = 0;
   int u_first = 0;                   // first sequence of this workgroup
@@ -292,18 +292,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
       const int ctx = p.ctx[b];
       sum += ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
     }
-    s_part[threadIdx.x] = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int run = 0;
-      for (int t = 0; t < nthreads; ++t) {
-        const int v = s_part[t];
-        s_part[t] = run;
-        run += v;
-      }
+    // exclusive prefix over the threads: a scan inside each wave, then the
+    // totals of the waves before (integer adds, so the order is free)
+    const int ln = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (ln >= d) incl += v;
     }
+    if (ln == kWave - 1) s_part[wv] = incl;
     __syncthreads();
-    int run = s_part[threadIdx.x];
+    int run = incl - sum;
+    for (int w2 = 0; w2 < wv; ++w2) run += s_part[w2];
     for (int b = b0; b < min(p.C, b0 + per); ++b) {
       s_off[b] = run;
       const int ctx = p.ctx[b];
