@@ -30,6 +30,7 @@
 #include "isd_common.hpp"
 
 #include <algorithm>
+#include <type_traits>
 #include <climits>
 
 namespace isd {
@@ -600,33 +601,41 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   f32x4 acc[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < n; j0 += kBatch) {
-    float mv[kBatch], lv[kBatch];
-    f32x4 ov[kBatch][kV];
-    bool has[kBatch];
+  // batches of B pieces, B the smallest of 2, 4, 8 that holds n (the same
+  // arithmetic for every B: one online step per piece, in order)
+  auto merge_all = [&](auto batch) {
+    constexpr int B = decltype(batch)::value;
+    for (int j0 = 0; j0 < n; j0 += B) {
+      float mv[B], lv[B];
+      f32x4 ov[B][kV];
+      bool has[B];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      has[j] = j0 + j < n && !empty(j0 + j);
-      const size_t idx = piece(has[j] ? j0 + j : 0);  // piece 0 always exists
-      mv[j] = p.part_ml[idx * 2];
-      lv[j] = p.part_ml[idx * 2 + 1];
-      const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
+      for (int j = 0; j < B; ++j) {
+        has[j] = j0 + j < n && !empty(j0 + j);
+        const size_t idx = piece(has[j] ? j0 + j : 0);  // piece 0 always exists
+        mv[j] = p.part_ml[idx * 2];
+        lv[j] = p.part_ml[idx * 2 + 1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + idx * D + d0);
 #pragma unroll
-      for (int k = 0; k < kV; ++k) ov[j][k] = src[k];
+        for (int k = 0; k < kV; ++k) ov[j][k] = src[k];
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (!has[j]) continue;
+        const float m_new = fmaxf(m_run, mv[j]);
+        const float a = fast_exp2(m_run - m_new), c = fast_exp2(mv[j] - m_new);
+        l_run = fmaf(l_run, a, lv[j] * c);
+#pragma unroll
+        for (int k = 0; k < kV; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(acc[k][e], a, ov[j][k][e] * c);
+        m_run = m_new;
+      }
     }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (!has[j]) continue;
-      const float m_new = fmaxf(m_run, mv[j]);
-      const float a = fast_exp2(m_run - m_new), c = fast_exp2(mv[j] - m_new);
-      l_run = fmaf(l_run, a, lv[j] * c);
-#pragma unroll
-      for (int k = 0; k < kV; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[k][e] = fmaf(acc[k][e], a, ov[j][k][e] * c);
-      m_run = m_new;
-    }
-  }
+  };
+  if (n <= 2) merge_all(std::integral_constant<int, 2>{});
+  else if (n <= 4) merge_all(std::integral_constant<int, 4>{});
+  else merge_all(std::integral_constant<int, kBatch>{});
   const int hl = col / p.rows, i = col % p.rows;
   const int h = g * p.group + hl;
   f32x4* dst = reinterpret_cast<f32x4*>(p.out + ((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d0);
