@@ -16,7 +16,13 @@ accept step over the block logits (verify, residual / bonus draw, proposals,
 KV commit). The MLP and the LM head are not part of the library; the logits
 the LM head would produce are synthetic and pre-generated per step.
 
+--workload 32b runs the same step at 32B-class shapes instead: C = 16
+sequences of 16,384 cached tokens, 64 layers of 64 query / 8 KV heads,
+head_dim 128, hidden 5120 (Q|K|V 10240 wide, O from 8192 to 5120), with the
+stride (--N) and the acceptance (--accept) of one cell of the stride sweep.
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                       [--workload 8b|32b] [--N N] [--accept P]
 Prints one JSON line.
 """
 
@@ -39,6 +45,7 @@ PROBE_EVERY = 8  # timed steps between the ones bracketed with HIP events
 
 CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, lora_rank=32,
            ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3, proposal="sample")
+CFG_32B = dict(CFG, C=16, Hq=64, Hkv=8, D=128, layers=64, hidden=5120, ctx=16384)
 
 
 def log(*a):
@@ -73,13 +80,14 @@ def projection_flops(cfg):
     C, N, H, r = cfg["C"], cfg["N"], cfg["hidden"], cfg["lora_rank"]
     M, Mm = C * 2 * N, C * N
     n_qkv = (cfg["Hq"] + 2 * cfg["Hkv"]) * cfg["D"]
+    n_att = cfg["Hq"] * cfg["D"]  # width of the attention output (input of O)
     lora = cfg.get("lora", "gated") == "gated"
-    qkv = 2 * M * H * n_qkv + lora * 3 * 2 * Mm * r * (H + n_qkv // 3)
-    o = 2 * M * H * H + lora * 2 * Mm * r * (H + H)
+    qkv = 2 * M * H * n_qkv + lora * 2 * Mm * r * (3 * H + n_qkv)  # three A [r, H]; B rows sum to n_qkv
+    o = 2 * M * n_att * H + lora * 2 * Mm * r * (n_att + H)
     return qkv, o
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_hbm_traffic_c64_n4.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_hbm_traffic_c64_n4.txt")  # default workload only
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verify_decoding_amd", "csrc", f)
                   for f in ("isd_attention.hip", "isd_common.hpp")]
 
@@ -149,6 +157,7 @@ def build(cfg, steps_total, dev):
     del src
 
     M, H, r = C * R, cfg["hidden"], cfg["lora_rank"]
+    HD = Hq * D  # attention output width, the O projection's input
     mask = torch.from_numpy(workload.stride_mask(M, N).astype(np.uint8)).to(dev)
     layers = []
     for l in range(L):
@@ -157,7 +166,7 @@ def build(cfg, steps_total, dev):
             k=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "kb", l),
             v=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "vb", l),
             x=workload.normal((M, H), 1.0, torch.bfloat16, dev, seed, "x", l),
-            xo=workload.normal((M, H), 1.0, torch.bfloat16, dev, seed, "xo", l),
+            xo=workload.normal((M, HD), 1.0, torch.bfloat16, dev, seed, "xo", l),
             out=torch.empty((C, R, Hq, D), dtype=torch.float32, device=dev),
         )
         # Q, K and V run as one projection (weights stacked, 6144 outputs);
@@ -178,8 +187,8 @@ def build(cfg, steps_total, dev):
             off += nout
         proj["qkv"] = dict(W=torch.cat(Ws).contiguous(), A=torch.cat(As).contiguous(), B=Bqkv,
                            y=torch.empty((M, n_qkv), dtype=torch.float32, device=dev))
-        proj["o"] = dict(W=workload.normal((H, H), 0.02, torch.bfloat16, dev, seed, "W", "o", l),
-                         A=workload.normal((r, H), 0.01, torch.bfloat16, dev, seed, "A", "o", l),
+        proj["o"] = dict(W=workload.normal((H, HD), 0.02, torch.bfloat16, dev, seed, "W", "o", l),
+                         A=workload.normal((r, HD), 0.01, torch.bfloat16, dev, seed, "A", "o", l),
                          B=workload.normal((H, r), 0.01, torch.bfloat16, dev, seed, "B", "o", l),
                          y=torch.empty((M, H), dtype=torch.float32, device=dev))
         lay["proj"] = proj
@@ -221,14 +230,15 @@ def dry_run(cfg, steps_total, ctx0, dev):
     return logits, np.array(ctxs), np.array(nds), np.array(accs), final_ctx
 
 
-def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14):
+def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=None):
     """The oracle, as it stands, on a bounded sample of the same workload
     (about 10 s on 16 host cores): (a) block attention + gated Q/K/V/O
-    projections, all 36 layers, for `fwd_seqs` sequences with contexts drawn
-    from the workload's distribution; (b) the accept step for `accept_seqs`
-    sequences over `accept_steps` steps from FRESH at the full vocabulary.
-    Returns tokens/s of one sequence-step (forward + accept) scaled by the
-    tokens it emits."""
+    projections of every layer (or of the first `layers_timed`, scaled to
+    all of them) for `fwd_seqs` sequences with contexts drawn from the
+    workload's distribution; (b) the accept step for `accept_seqs` sequences
+    over `accept_steps` steps from FRESH at the full vocabulary. Returns
+    tokens/s of one sequence-step (forward + accept) scaled by the tokens it
+    emits."""
     import workload
     from oracle import accept as oacc
     from oracle import attention as oatt
@@ -244,9 +254,10 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14):
     R, H, r = 2 * N, cfg["hidden"], cfg["lora_rank"]
     ctxs = workload.contexts(cfg["seed"], C, cfg["ctx"])[:fwd_seqs]
     L = cfg["layers"]
+    Lt = layers_timed or L
 
     t_fwd = 0.0
-    for l in range(L * fwd_seqs):
+    for l in range(Lt * fwd_seqs):
         case = workload.AttentionCase(cfg["seed"] + 100 + l, C=1, rows=R, Hq=Hq, Hkv=Hkv, D=D,
                                       ctx=int(ctxs[l % fwd_seqs]))
         kp = np.zeros((case.num_pages, 16, Hkv, D))
@@ -255,8 +266,8 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14):
                       case.lengths)
         q = case.q.double().numpy()
         mats = []
-        for name, nout in (("q", Hq * D), ("k", Hkv * D), ("v", Hkv * D), ("o", H)):
-            x, W, A, B = (t.double().numpy() for t in workload.lora_case(cfg["seed"] + l // fwd_seqs, R, H, nout, r))
+        for name, kin, nout in (("q", H, Hq * D), ("k", H, Hkv * D), ("v", H, Hkv * D), ("o", Hq * D, H)):
+            x, W, A, B = (t.double().numpy() for t in workload.lora_case(cfg["seed"] + l // fwd_seqs, R, kin, nout, r))
             mats.append((x, W, A, B))
         mask = workload.stride_mask(R, N)
         t0 = time.perf_counter()
@@ -264,7 +275,7 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14):
         for x, W, A, B in mats:
             olora.gated_lora(x, W, A, B, mask, 1.0)
         t_fwd += time.perf_counter() - t0
-    t_fwd_seq_step = t_fwd / fwd_seqs
+    t_fwd_seq_step = t_fwd / fwd_seqs * L / Lt
 
     sigma_q = workload.SIGMA_Q_V151936[cfg["accept"]]
     teacher = workload.TeacherLogits(cfg["seed"], accept_seqs, V, accept_steps * N + R + 1, cfg["sigma_l"],
@@ -290,8 +301,10 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14):
     t_step = t_fwd_seq_step + t_acc / seq_steps
     tok_per_seq_step = tokens / seq_steps
     value = tok_per_seq_step / t_step
-    sample = (f"oracle (numpy fp64): attention + gated Q/K/V/O projections, all {L} layers, of "
-              f"{fwd_seqs} sequences (contexts {int(ctxs.min())}..{int(ctxs.max())}), "
+    ctx_note = f"contexts {int(ctxs.min())}..{int(ctxs.max())}" if ctxs.min() != ctxs.max() else f"context {int(ctxs[0])}"
+    layer_note = f"all {L} layers" if Lt == L else f"{Lt} of {L} layers timed and scaled to {L}"
+    sample = (f"oracle (numpy fp64): attention + gated Q/K/V/O projections, {layer_note}, of "
+              f"{fwd_seqs} sequences ({ctx_note}), "
               f"{t_fwd_seq_step:.2f} s per sequence-step; accept for {accept_seqs} sequences x "
               f"{accept_steps} steps from FRESH at V={V}, {t_acc / seq_steps * 1e3:.1f} ms per "
               f"sequence-step, {tok_per_seq_step:.3f} tokens per sequence-step; "
@@ -305,10 +318,10 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--slices", type=int, default=-64,
-                    help="attention split: -T = batch-invariant chunks of T 32-key tiles (default: 64, the "
-                         "lossless R-ISD configuration); 0 = stream-K with automatic slices; S > 0 = stream-K "
-                         "with S workgroups per KV-head group")
+    ap.add_argument("--slices", type=int, default=None,
+                    help="attention split: -T = batch-invariant chunks of T 32-key tiles (the lossless R-ISD "
+                         "configuration; default T = 64 for 8b, 66 for 32b); 0 = stream-K with automatic "
+                         "slices; S > 0 = stream-K with S workgroups per KV-head group")
     ap.add_argument("--proposal", choices=("sample", "argmax"), default="sample",
                     help="draft proposals: sampled from q (default) or argmax q")
     ap.add_argument("--lora", choices=("gated", "off"), default="gated",
@@ -317,11 +330,23 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (two graphs: even and odd steps); every "
                          f"{PROBE_EVERY}th timed step runs eagerly with the event probes")
+    ap.add_argument("--workload", choices=("8b", "32b"), default="8b",
+                    help="8b: C=64 ragged 1k-8k contexts, 36 layers (default); 32b: C=16 contexts of 16,384, "
+                         "64 layers of 64/8 heads, hidden 5120")
+    ap.add_argument("--N", type=int, default=4, help="stride N (2N-row blocks); default 4")
+    ap.add_argument("--accept", type=float, default=0.9, choices=(0.5, 0.7, 0.9),
+                    help="mean per-draft acceptance the draft noise is set for; default 0.9")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print per-kernel means of a rocprofv3 --pmc CSV output directory and exit")
     args = ap.parse_args()
+    if args.slices is None:
+        # The chunk size is a deployment constant picked for the context mix:
+        # at 16,384-token contexts, 66 tiles give 8 chunks per sequence and
+        # 16 x 8 x 2 head groups = 256 workgroups, one round on 256 CUs
+        # (64 tiles would give a ninth, one-tile chunk and 288 workgroups).
+        args.slices = -64 if args.workload == "8b" else -66
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return
@@ -342,7 +367,9 @@ def main():
 
     import draft_verify_decoding_amd as dvd
 
-    cfg = dict(CFG, proposal=args.proposal, lora=args.lora)
+    cfg = dict(CFG if args.workload == "8b" else CFG_32B, proposal=args.proposal, lora=args.lora, N=args.N,
+               accept=args.accept)
+    default_workload = args.workload == "8b" and args.N == 4
     dev = "cuda"
     torch.cuda.set_device(0)
     dvd.lib()
@@ -523,7 +550,8 @@ def main():
     att_only_tps = probe_tokens / ((np.sum(att_ms) + np.sum(acc_ms)) / 1e3)
 
     res = {
-        "metric": METRIC,
+        "metric": (METRIC if args.workload == "8b" else
+                   f"ISD accepted tokens/s at C={C},N={N} (32B shapes); attn+accept HBM GB/s vs peak"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -536,10 +564,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "stationary batch C=64, N=4 (8-row blocks), 8B-class GQA 32/8 heads, head_dim 128, "
-                        "36 layers, bf16 paged KV (16-token pages), contexts U{1024..8192}, vocab 151936, "
-                        "acceptance ~0.9, " + ("gated-LoRA rank-32" if args.lora == "gated" else "base (no LoRA)")
-                        + " Q/K/V/O projections; MLP and LM head not included",
+            "workload": (f"stationary batch C={C}, N={N} ({R}-row blocks), "
+                         + ("8B-class GQA 32/8 heads, head_dim 128, 36 layers, hidden 4096, "
+                            if args.workload == "8b" else
+                            "32B-class GQA 64/8 heads, head_dim 128, 64 layers, hidden 5120, ")
+                         + "bf16 paged KV (16-token pages), "
+                         + ("contexts U{1024..8192}" if args.workload == "8b" else "contexts 16384")
+                         + f", vocab 151936, acceptance ~{cfg['accept']}, "
+                         + ("gated-LoRA rank-32" if args.lora == "gated" else "base (no LoRA)")
+                         + " Q/K/V/O projections; MLP and LM head not included"),
             "C": C, "N": N, "layers": L, "Hq": Hq, "Hkv": cfg["Hkv"], "head_dim": D, "vocab": V,
             "global_batch": C, "seq_len": int(np.mean(ctxs[W])), "parallelism": "none (1 GPU)",
             "proposal": cfg["proposal"],
@@ -575,7 +608,7 @@ def main():
     proj_tflops = (qkv_flops + o_flops) * len(probes) * L / ((np.sum(qkv_ms) + np.sum(o_ms)) / 1e3) / 1e12
     res["projection_mfma"] = {"achieved": round(float(proj_tflops), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(float(proj_tflops) / MFMA_BF16_PEAK_TFLOPS, 4)}
-    rec = committed_traffic()
+    rec = committed_traffic() if default_workload else None
     if rec is not None:
         # counter bytes per call of the profiled run, and their ratio to that
         # run's algorithmic bytes (contexts grow a little over a run)
@@ -584,7 +617,8 @@ def main():
         res["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
-        res["cpu_baseline"] = cpu_baseline(cfg)
+        res["cpu_baseline"] = (cpu_baseline(cfg) if args.workload == "8b" else
+                               cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14, layers_timed=8))
         log(f"[bench] cpu baseline took {time.perf_counter() - t_cpu:.1f} s")
     print(json.dumps(res), flush=True)
 

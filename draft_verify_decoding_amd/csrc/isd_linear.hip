@@ -30,6 +30,8 @@ constexpr int kBK = 64;
 constexpr int kXcds = 8;  // XCDs of an MI355X
 
 constexpr int kMaxSplits = 8;  // split-K shares of U = x A^T
+constexpr int kMaxStages = 6;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 
 // The LoRA delta of one 32x32 output block, U B^T, on bf16 MFMA: each U row
 // (fp32) is split into a bf16 high part (truncation) and the bf16 rounding
@@ -155,10 +157,21 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   constexpr int STAGE = (BM + BN) * kBK;                // elements per stage
   // one LDS object per stage, so the compiler can tell that reading a stage
   // does not wait for the direct loads into the others
-  static_assert(STAGES == 3 || STAGES == 4, "three or four stages");
-  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGES == 4 ? STAGE : 8];
+  static_assert(STAGES >= 3 && STAGES <= kMaxStages, "stage count");
+  static_assert(STAGES * STAGE * 2 <= kLdsBytes, "stages fit the LDS");
+#define ISD_STAGE(i) __shared__ __attribute__((aligned(16))) uint16_t st##i[STAGES > i ? STAGE : 8];
+  ISD_STAGE(0) ISD_STAGE(1) ISD_STAGE(2) ISD_STAGE(3) ISD_STAGE(4) ISD_STAGE(5)
+#undef ISD_STAGE
+  // (stages past STAGES are never named, so they take no LDS)
   auto stage_ptr = [&](int stage) -> uint16_t* {
-    return stage == 0 ? st0 : (stage == 1 ? st1 : (stage == 2 ? st2 : st3));
+    switch (stage) {
+#define ISD_CASE(i) \
+  case i:           \
+    if constexpr (STAGES > i) return st##i;
+      ISD_CASE(1) ISD_CASE(2) ISD_CASE(3) ISD_CASE(4) ISD_CASE(5)
+#undef ISD_CASE
+      default: return st0;
+    }
   };
 
   const int tid = threadIdx.x;
@@ -303,7 +316,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   // unrolled over kUnroll slabs: the compiler proves that reading one stage
   // need not wait for the loads into the others only inside one trip of the
   // loop, and waits for every load once per trip
-  constexpr int kUnroll = 4 * STAGES;
+  constexpr int kUnroll = STAGES * ((16 + STAGES - 1) / STAGES);
   for (int kt0 = 0; kt0 < nk; kt0 += kUnroll) {
 #pragma unroll
     for (int dd = 0; dd < kUnroll; ++dd) {
@@ -460,15 +473,18 @@ using namespace isd;
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // Tile choice depends only on (M, Nout) and the CU count, never on the
-// data, and every choice gives each output the same reduction order. The
-// largest wave tile whose workgroups still cover every CU wins (fewer LDS
-// bytes per MFMA); those run one workgroup per CU with four LDS stages.
-// Otherwise 64 x 64 tiles, three stages, three workgroups per CU.
-template <int TM, int TN, int R16>
+// data, and every choice gives each output the same reduction order. A CU
+// streams its workgroups' operand slabs at a rate of its own that the chip
+// seldom saturates (the weights come from HBM, the rows of x from L2), so
+// the choice minimises the bytes of the busiest CU, rounds of workgroups
+// per CU x (BM + BN) rows per slab; on a tie the earlier (larger) tile wins
+// (fewer LDS bytes per MFMA). The large tiles run one workgroup per CU with
+// four stages; 64 x 64 tiles take five (two workgroups per CU), or three
+// for the split-K partials of U.
+template <int TM, int TN, int STAGES, int R16>
 hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
   const long tiles = static_cast<long>((p.M + 64 * TM - 1) / (64 * TM)) * ((p.Nout + 64 * TN - 1) / (64 * TN));
-  constexpr int stages = (TM * TN > 1) ? 4 : 3;
-  hipLaunchKernelGGL((gemm_nt_kernel<TM, TN, stages, R16>), dim3(static_cast<unsigned>(tiles * p.splits)),
+  hipLaunchKernelGGL((gemm_nt_kernel<TM, TN, STAGES, R16>), dim3(static_cast<unsigned>(tiles * p.splits)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -476,15 +492,26 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
 template <int R16>
 hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   const long cus = isd_device_cus_internal();
-  auto tiles = [&](int tm, int tn) {
-    return static_cast<long>((p.M + 64 * tm - 1) / (64 * tm)) * ((p.Nout + 64 * tn - 1) / (64 * tn));
-  };
-  if (p.splits == 1) {
-    if (tiles(2, 2) >= cus) return launch_tile<2, 2, R16>(p, stream);
-    if (tiles(1, 3) >= cus) return launch_tile<1, 3, R16>(p, stream);
-    if (tiles(1, 2) >= cus) return launch_tile<1, 2, R16>(p, stream);
+  constexpr int kShapes[4][2] = {{1, 3}, {2, 2}, {1, 2}, {1, 1}};
+  int pick = 3;
+  long best = -1;
+  for (int i = p.splits == 1 ? 0 : 3; i < 4; ++i) {
+    const int tm = kShapes[i][0], tn = kShapes[i][1];
+    const long wgs = static_cast<long>((p.M + 64 * tm - 1) / (64 * tm)) * ((p.Nout + 64 * tn - 1) / (64 * tn)) * p.splits;
+    const long cost = (wgs + cus - 1) / cus * (64 * tm + 64 * tn);
+    if (best < 0 || cost < best) {
+      best = cost;
+      pick = i;
+    }
   }
-  return launch_tile<1, 1, R16>(p, stream);
+  if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
+    if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
+  switch (pick) {
+    case 0: return launch_tile<1, 3, 4, R16>(p, stream);
+    case 1: return launch_tile<2, 2, 4, R16>(p, stream);
+    case 2: return launch_tile<1, 2, 4, R16>(p, stream);
+    default: return launch_tile<1, 1, 5, R16>(p, stream);
+  }
 }
 
 hipError_t launch_gemm(const GemmParams& p, int r, hipStream_t stream) {

@@ -72,6 +72,32 @@ def test_gated_lora_8b_shapes(Nout, r):
     assert torch.equal(f.view(torch.int32), sep.cpu().view(torch.int32))
 
 
+@pytest.mark.parametrize("K,Nout,r", [(5120, 10240, 96), (8192, 5120, 32)])
+def test_gated_lora_32b_shapes(K, Nout, r):
+    """32B-class projections of a C=16, N=4 step (128 rows, hidden 5120):
+    fused Q|K|V (64 + 2 x 8 heads of 128 = 10240 wide, r = 3 x 32) and O
+    (8192 -> 5120). These sizes pick other tiles than the 8B ones; a row
+    block computed alone (another tile again) keeps the same bits."""
+    M = 128
+    x, W, A, B, mask = case(7, M, K, Nout, r)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    base = dvd.isd_linear(xd, Wd)
+    fused = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=1.0)
+    sep = base.clone()
+    dvd.gated_lora_apply(xd, Ad, Bd, md, sep, scale=1.0)
+    alone = dvd.isd_linear_gated(xd[40:48].contiguous(), Wd, Ad, Bd, md[40:48].contiguous(), scale=1.0)
+    torch.cuda.synchronize()
+    want = ref.gated_lora(x.double().numpy(), W.double().numpy(), A.double().numpy(),
+                          B.double().numpy(), mask, 1.0)
+    f = fused.cpu()
+    assert rel_err(f.double().numpy(), want) < 2e-3
+    m = torch.from_numpy(mask)
+    assert torch.equal(f[~m].view(torch.int32), base.cpu()[~m].view(torch.int32))
+    assert torch.equal(f.view(torch.int32), sep.cpu().view(torch.int32))
+    assert torch.equal(alone.cpu().view(torch.int32), f[40:48].view(torch.int32))
+
+
 def test_reduction_order_does_not_depend_on_rows_or_tile():
     """Row results of isd_linear are the same bits whether the row is
     computed with 511 others, alone, or in a small launch that picks the
