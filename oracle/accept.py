@@ -50,6 +50,23 @@ def row_stats(row):
     return m, float(np.exp(row - m).sum())
 
 
+def chunk_stats(row, chunk):
+    """(max, sum of exp(l - max)) of each run of `chunk` consecutive entries
+    of one logits row (the last run may be shorter), float64, shape [n, 2].
+
+    The softmax normaliser of the row is a sum over its entries, so it splits
+    over any partition of the vocabulary: with M the row maximum,
+    sum_v exp(l_v - M) = sum_c exp(m_c - M) * s_c for the runs' (m_c, s_c).
+    Computing the runs where the logits are produced (the LM-head GEMM) is
+    the same quantity as row_stats, re-associated.
+    """
+    row = np.asarray(row, dtype=np.float64)
+    out = []
+    for c0 in range(0, row.shape[0], chunk):
+        out.append(row_stats(row[c0:c0 + chunk]))
+    return np.array(out, dtype=np.float64)
+
+
 def inv_cdf(w, u):
     """Smallest index v with sum_{v' <= v} w[v'] > u * sum(w).
 

@@ -420,3 +420,32 @@ def test_block_assemble_feeds_the_cache_every_emitted_token_once(N):
         assert (is_mask.sum(1) == np.where(n == N - 1, N, 2 * N - 1)).all()
     for b in range(C):
         assert committed[b] == emitted[b][:-1]
+
+
+# ------------------------------------------------- chunked softmax statistics
+
+def test_chunk_stats_brute_force_and_row_normaliser():
+    """Per-run (max, sum exp(l - max)) by plain loops, the last run short;
+    merged over the runs they give the row's own softmax normaliser."""
+    import math
+    rng = np.random.default_rng(11)
+    for V, chunk in ((37, 8), (64, 16), (100, 100), (5, 8)):
+        row = rng.normal(0.0, 3.0, V) + 40.0  # large logits: the shift by the max matters
+        got = accept.chunk_stats(row, chunk)
+        assert got.shape == (-(-V // chunk), 2)
+        for c in range(got.shape[0]):
+            part = [float(x) for x in row[c * chunk:(c + 1) * chunk]]
+            m = max(part)
+            s = math.fsum(math.exp(x - m) for x in part)
+            assert got[c, 0] == m
+            assert abs(got[c, 1] - s) <= 1e-12 * s
+        M = float(np.max(row))
+        merged = math.fsum(math.exp(m - M) * s for m, s in got)
+        assert abs(merged - math.fsum(math.exp(float(x) - M) for x in row)) <= 1e-12 * merged
+
+
+def test_chunk_stats_special_cases():
+    """Equal entries give (value, count); -inf entries add nothing."""
+    got = accept.chunk_stats(np.array([2.0, 2.0, 2.0, -np.inf, 1.0, -np.inf]), 3)
+    assert got[0, 0] == 2.0 and got[0, 1] == 3.0
+    assert got[1, 0] == 1.0 and got[1, 1] == 1.0
