@@ -230,6 +230,57 @@ def dry_run(cfg, steps_total, ctx0, dev):
     return logits, np.array(ctxs), np.array(nds), np.array(accs), final_ctx
 
 
+def lm_head_leg(cfg, dev, calls=20):
+    """isd_lm_head at the step's shape (C*2N rows, hidden, vocabulary) on
+    seeded random weights, timed with HIP events after the timed steps; and
+    isd_accept on its logits (FRESH state) with and without the chunk
+    statistics it produced, which is the statistics pass the LM head saves.
+    The step itself keeps the teacher's logits: random weights cannot give
+    the calibrated acceptance."""
+    import draft_verify_decoding_amd as dvd
+    import workload
+
+    C, N, H, V = cfg["C"], cfg["N"], cfg["hidden"], cfg["V"]
+    M = C * 2 * N
+    W = workload.normal((V, H), 3.0 / H ** 0.5, torch.bfloat16, dev, cfg["seed"], "lm-W")
+    h = workload.normal((M, H), 1.0, torch.bfloat16, dev, cfg["seed"], "lm-h")
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    nch = (V + 8191) // 8192
+    stats = torch.empty((M, nch, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(dvd.isd_lm_head_workspace_size(M, V), dtype=torch.uint8, device=dev)
+    call = dvd.prepare_lm_head(h, W, logits, stats, ws)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    us = timed(call, calls)
+    s_in, s_out = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
+    acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, 2 * N), dtype=torch.uint8, device=dev)
+    acc_out = dvd.AcceptOutputs(C, N, 2 * N, dev, diag=False)
+    lg3, st3 = logits.view(C, 2 * N, V), stats.view(C, 2 * N, nch, 2)
+    own = timed(lambda: dvd.isd_accept(lg3, None, s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws), calls)
+    given = timed(lambda: dvd.isd_accept(lg3, None, s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws,
+                                         chunk_stats=st3), calls)
+    flops = 2.0 * M * H * V
+    wbytes = V * H * 2
+    res = {"shape": f"{M} x {H} -> {V}", "us_per_call": round(us, 2),
+           "achieved_tflops": round(flops / us / 1e6, 1), "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "weight_gbps": round(wbytes / us / 1e3, 1),
+           "accept_fresh_us_own_stats": round(own, 2), "accept_fresh_us_lm_head_stats": round(given, 2)}
+    del W, h, logits, stats, ws
+    return res
+
+
 def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=None):
     """The oracle, as it stands, on a bounded sample of the same workload
     (about 10 s on 16 host cores): (a) block attention + gated Q/K/V/O
@@ -336,6 +387,8 @@ def main():
     ap.add_argument("--N", type=int, default=4, help="stride N (2N-row blocks); default 4")
     ap.add_argument("--accept", type=float, default=0.9, choices=(0.5, 0.7, 0.9),
                     help="mean per-draft acceptance the draft noise is set for; default 0.9")
+    ap.add_argument("--no-lm-head", action="store_true",
+                    help="skip the LM-head leg (isd_lm_head timed after the steps; not part of the step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -615,6 +668,10 @@ def main():
         res["roofline"]["traffic"] = rec["hbm_bytes_per_call"]
         res["roofline"]["traffic_over_algorithmic"] = rec["ratio_to_algorithmic"]
         res["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)
+    if not args.no_lm_head:
+        del logits[:]
+        torch.cuda.empty_cache()
+        res["lm_head"] = lm_head_leg(cfg, dev)
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
         res["cpu_baseline"] = (cpu_baseline(cfg) if args.workload == "8b" else

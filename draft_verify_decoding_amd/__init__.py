@@ -70,6 +70,7 @@ class IsdAcceptArgs(ctypes.Structure):
         ("dev_err", ctypes.c_void_p),
         ("proposal", ctypes.c_int32),
         ("step_dev", ctypes.c_void_p),
+        ("chunk_stats", ctypes.c_void_p),
     ]
 
 
@@ -103,6 +104,10 @@ _SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "isd_lm_head_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int]),
+    "isd_lm_head": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -250,13 +255,15 @@ class AcceptOutputs:
 
 
 def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
-               diag=False, dev_err=None, ctx=None, stream=None, proposal="sample", step_dev=None):
+               diag=False, dev_err=None, ctx=None, stream=None, proposal="sample", step_dev=None,
+               chunk_stats=None):
     """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
     AcceptOutputs (device tensors) and writes state_out. If ctx (int32 [C])
     is given, the kernel adds kv_commit to it. proposal: "sample" or
     "argmax" (drafts = argmax of the MASK rows). step_dev: optional int64
     device tensor [1] holding the step number (then `step` is ignored), for
-    calls captured in a graph."""
+    calls captured in a graph. chunk_stats: optional fp32 [C, rows, nch, 2]
+    from isd_lm_head (then the statistics pass is skipped)."""
     C, rows, ld = logits.shape
     V = ld if V is None else V
     if out is None:
@@ -284,6 +291,7 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     args.dev_err = None if dev_err is None else dev_err.data_ptr()
     args.proposal = PROPOSE[proposal]
     args.step_dev = None if step_dev is None else step_dev.data_ptr()
+    args.chunk_stats = None if chunk_stats is None else chunk_stats.data_ptr()
     _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
     return out
 
@@ -345,6 +353,35 @@ def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=Non
                                 _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "isd_linear_gated")
     return y
+
+
+def isd_lm_head_workspace_size(M, V):
+    return int(lib().isd_lm_head_workspace_size(M, V))
+
+
+def isd_lm_head(h, W, logits=None, chunk_stats=None, ws=None, stream=None):
+    """logits [M, ld] (torch.bfloat16) = h W^T, rounded to nearest even, and
+    their chunk statistics [M, nch, 2] fp32 (nch = ceil(V / 8192))."""
+    M, K = h.shape
+    V = W.shape[0]
+    if logits is None:
+        logits = torch.empty((M, V), dtype=torch.bfloat16, device=h.device)
+    nch = (V + 8191) // 8192
+    if chunk_stats is None:
+        chunk_stats = torch.empty((M, nch, 2), dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws = torch.empty(isd_lm_head_workspace_size(M, V), dtype=torch.uint8, device=h.device)
+    rc = lib().isd_lm_head(_p(h), _p(W), M, K, V, _p(logits), logits.stride(-2), _p(chunk_stats), _p(ws),
+                           ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "isd_lm_head")
+    return logits, chunk_stats
+
+
+def prepare_lm_head(h, W, logits, chunk_stats, ws, stream=None):
+    M, K = h.shape
+    V = W.shape[0]
+    return Prepared("isd_lm_head", _p(h), _p(W), M, K, V, _p(logits), logits.stride(-2), _p(chunk_stats), _p(ws),
+                    ws.numel() * ws.element_size(), _stream(stream), keep=(h, W, logits, chunk_stats, ws))
 
 
 # ------------------------------------------------------- prepared calls

@@ -27,7 +27,7 @@
 
 namespace isd {
 
-constexpr int kChunk = 8192;     // vocab entries per stats chunk
+constexpr int kChunk = kVocabChunk;  // vocab entries per stats chunk
 constexpr int kThreads = 256;    // threads per workgroup
 constexpr int kPerThread = 32;   // entries per thread in a chunk
 constexpr int kStatsChunks = 2;  // chunks per workgroup of the stats launch
@@ -51,6 +51,7 @@ struct AcceptParams {
   int* arrive;      // [C] workgroups of the sample launch done, per sequence
   int32_t* dev_err;
   int argmax;       // proposals are argmax q (a point mass at the draft)
+  int stats_given;  // stats come from the caller (isd_lm_head): no statistics pass
 };
 
 // ------------------------------------------- values handed between workgroups
@@ -103,23 +104,8 @@ __device__ __forceinline__ float uniform_of(uint64_t w0) {
 }
 
 // -------------------------------------------------------------- arithmetic
-// Unnormalised softmax weight relative to the row max M (as exp2 of a
-// log2-scaled argument). Every place that needs P(x) uses these helpers so
-// that equal inputs give equal bits.
-__device__ __forceinline__ float weight_of(float l, float m_log2) { return fast_exp2(fmaf(l, kLog2e, -m_log2)); }
-__device__ __forceinline__ float prob_of(float l, float M, float S) { return weight_of(l, M * kLog2e) / S; }
-
-// Merge two (max, sum exp(l - max)) pairs.
-__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
-  const float mm = fmaxf(m, m2);
-  if (mm == -INFINITY) {
-    m = mm;
-    s = 0.f;
-    return;
-  }
-  s = s * fast_exp2((m - mm) * kLog2e) + s2 * fast_exp2((m2 - mm) * kLog2e);
-  m = mm;
-}
+// weight_of, prob_of and merge_ms (isd_common.hpp) are the only places that
+// turn logits into softmax weights, so equal inputs give equal bits.
 
 template <typename E>
 __device__ __forceinline__ const E* row_ptr(const void* base, long ld, int rows, int b, int r) {
@@ -259,6 +245,13 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) 
     block_reduce_ms(m, s);
     if (threadIdx.x == 0 && c0 + h < p.nch) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c0 + h] = make_float2(m, s);
   }
+}
+
+// With the chunk statistics given, only the arrival counters of the sample
+// launch need clearing.
+__global__ __launch_bounds__(256) void accept_arrive_reset_kernel(int* arrive, int C) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < C) arrive[b] = 0;
 }
 
 // ------------------------------------------------ shared per-sequence logic
@@ -728,8 +721,11 @@ bool state_ok(const isd_seq_state& s) { return s.n_draft && s.drafts && s.q_x &&
 
 template <typename E>
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_stats_kernel<E>, dim3((p.nch + kStatsChunks - 1) / kStatsChunks, 2 * p.N - 1, p.C),
-                     dim3(kThreads), 0, stream, p);
+  if (p.stats_given)
+    hipLaunchKernelGGL(accept_arrive_reset_kernel, dim3((p.C + 255) / 256), dim3(256), 0, stream, p.arrive, p.C);
+  else
+    hipLaunchKernelGGL(accept_stats_kernel<E>, dim3((p.nch + kStatsChunks - 1) / kStatsChunks, 2 * p.N - 1, p.C),
+                       dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(accept_sample_kernel<E>, dim3(p.ns, p.C), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -759,6 +755,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   const int esz = a->dtype == ISD_BF16 ? 2 : 4;
   if (a->ld < a->V || (a->ld * esz) % 16 != 0) return ISD_E_INVALID;
   if (!aligned16(a->logits) || (a->prev_logits && !aligned16(a->prev_logits))) return ISD_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(a->chunk_stats) & 7u) return ISD_E_INVALID;  // read as float pairs
   if (a->in.n_draft == a->out.n_draft || a->in.drafts == a->out.drafts || a->in.q_x == a->out.q_x ||
       a->in.q_m == a->out.q_m || a->in.q_s == a->out.q_s || a->in.q_row == a->out.q_row)
     return ISD_E_INVALID;
@@ -792,7 +789,9 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.row_m = a->row_m;
   p.row_s = a->row_s;
   char* ws = static_cast<char*>(a->ws);
-  p.stats = reinterpret_cast<float2*>(ws + L.stats_off);
+  p.stats_given = a->chunk_stats != nullptr;
+  p.stats = p.stats_given ? reinterpret_cast<float2*>(const_cast<float*>(a->chunk_stats))
+                          : reinterpret_cast<float2*>(ws + L.stats_off);
   p.resid = reinterpret_cast<float*>(ws + L.resid_off);
   p.samp = reinterpret_cast<int2*>(ws + L.samp_off);
   p.arrive = reinterpret_cast<int*>(ws + L.arrive_off);

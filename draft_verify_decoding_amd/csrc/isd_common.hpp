@@ -39,6 +39,28 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Vocabulary entries per chunk of the softmax statistics (max, sum of
+// exp(l - max)) that the accept step and the LM head exchange.
+constexpr int kVocabChunk = 8192;
+
+// Unnormalised softmax weight relative to the max M (as exp2 of a
+// log2-scaled argument). Every place that needs P(x) uses these helpers so
+// that equal inputs give equal bits.
+__device__ __forceinline__ float weight_of(float l, float m_log2) { return fast_exp2(fmaf(l, kLog2e, -m_log2)); }
+__device__ __forceinline__ float prob_of(float l, float M, float S) { return weight_of(l, M * kLog2e) / S; }
+
+// Merge two (max, sum exp(l - max)) pairs.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) {
+    m = mm;
+    s = 0.f;
+    return;
+  }
+  s = s * fast_exp2((m - mm) * kLog2e) + s2 * fast_exp2((m2 - mm) * kLog2e);
+  m = mm;
+}
+
 // Element type traits for the two storage types.
 template <typename E>
 struct Elem;

@@ -31,6 +31,8 @@ constexpr int kXcds = 8;  // XCDs of an MI355X
 
 constexpr int kMaxSplits = 8;  // split-K shares of U = x A^T
 constexpr int kMaxStages = 6;
+constexpr int kLogitsTileN = 128;  // columns per tile of the LM head (TN = 2), a divisor of the vocabulary chunk
+static_assert(kVocabChunk % kLogitsTileN == 0, "chunks are whole tiles");
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 
 // The LoRA delta of one 32x32 output block, U B^T, on bf16 MFMA: each U row
@@ -119,6 +121,11 @@ struct GemmParams {
   float scale;
   int M, K, Nout;
   int splits;           // K shares; split s runs slabs [s nk / splits, (s+1) nk / splits)
+  // logits epilogue (LM head): bf16 output and per-row tile statistics
+  uint16_t* yb;         // [M][ldy] bf16 bits
+  long ldy;
+  float2* tstats;       // [M][tiles_n] (max, sum exp(l - max)) of the tile's columns
+  int tiles_n;
 };
 
 // Wait until at most n vector-memory operations of this wave are in flight
@@ -149,7 +156,7 @@ __device__ __forceinline__ void load_lds16(const uint16_t* src, uint16_t* dst) {
 // a workgroup tile is 64 TM x 64 TN. Per 16-deep step a wave reads TM + TN
 // operand fragments (1 KB each) from LDS for TM * TN MFMAs: larger wave tiles
 // need less LDS bandwidth per MFMA, which is what bounds this loop.
-template <int TM, int TN, int STAGES, int R16>
+template <int TM, int TN, int STAGES, int R16, bool kLogits = false>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   constexpr int WM = 32 * TM, WN = 32 * TN;
   constexpr int BM = 2 * WM, BN = 2 * WN;
@@ -336,6 +343,64 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   }
   wait_vm_lgkm0<0>();
 
+  // LM head: the logits are rounded to bf16 (the values the accept step
+  // reads) and stored; per row, the (max, sum of exp(l - max)) of the
+  // tile's BN columns follows from those rounded values. Register e of lane
+  // (j, hh) is row 8(e/4) + 4hh + e%4 of the 32x32 block, column j: a
+  // butterfly over the 32 lanes of a half gives every lane the row's value
+  // (the pairs add the same two numbers, so all lanes agree), the TN blocks
+  // of a wave are combined first, and the two waves that share rows are
+  // merged through LDS, the left one first. Columns past Nout count as -inf.
+  if constexpr (kLogits) {
+    static_assert(R16 == 0, "the logits epilogue has no adapter");
+    float2* sms = reinterpret_cast<float2*>(stage_ptr(0));  // [BM][2]
+    static_assert(BM * 2 * 8 <= STAGE * 2, "row partials fit one stage");
+    stage_barrier();  // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m0 = m_blk + wm + 32 * i;
+      float xv[TN][16];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n_blk + wn + 32 * j + lane32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const uint32_t bits = f32_to_bf16_bits(acc[i][j][e]);
+          if (row < p.M && col < p.Nout) p.yb[static_cast<long>(row) * p.ldy + col] = static_cast<uint16_t>(bits);
+          xv[j][e] = col < p.Nout ? bf16_bits_to_f32(static_cast<uint16_t>(bits)) : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float m = xv[0][e];
+#pragma unroll
+        for (int j = 1; j < TN; ++j) m = fmaxf(m, xv[j][e]);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+        float sum = 0.f;
+        if (m != -INFINITY) {
+          const float ml = m * kLog2e;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) sum += weight_of(xv[j][e], ml);
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) sum += shfl_xor_f(sum, off);
+        if (lane32 == 0) sms[(wm + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * 2 + (wn != 0)] = make_float2(m, sum);
+      }
+    }
+    wait_vm_lgkm0<0>();
+    stage_barrier();
+    for (int r = tid; r < BM; r += 256) {
+      const int row = m_blk + r;
+      if (row >= p.M) break;
+      float m = sms[2 * r].x, sum = sms[2 * r].y;
+      merge_ms(m, sum, sms[2 * r + 1].x, sms[2 * r + 1].y);
+      p.tstats[static_cast<long>(row) * p.tiles_n + n_blk / BN] = make_float2(m, sum);
+    }
+    return;
+  }
+
   // Gated: the workgroup writes the U rows of its BM rows into LDS, reusing
   // the stages (rows padded by 4 floats so the fragment reads spread over the
   // banks); each wave then splits its rows once for all of its column blocks.
@@ -481,10 +546,10 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // (fewer LDS bytes per MFMA). The large tiles run one workgroup per CU with
 // four stages; 64 x 64 tiles take five (two workgroups per CU), or three
 // for the split-K partials of U.
-template <int TM, int TN, int STAGES, int R16>
+template <int TM, int TN, int STAGES, int R16, bool kLogits = false>
 hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
   const long tiles = static_cast<long>((p.M + 64 * TM - 1) / (64 * TM)) * ((p.Nout + 64 * TN - 1) / (64 * TN));
-  hipLaunchKernelGGL((gemm_nt_kernel<TM, TN, STAGES, R16>), dim3(static_cast<unsigned>(tiles * p.splits)),
+  hipLaunchKernelGGL((gemm_nt_kernel<TM, TN, STAGES, R16, kLogits>), dim3(static_cast<unsigned>(tiles * p.splits)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -512,6 +577,29 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
     case 2: return launch_tile<1, 2, 4, R16>(p, stream);
     default: return launch_tile<1, 1, 5, R16>(p, stream);
   }
+}
+
+// Chunk statistics of the logits from the tile statistics: one wave per
+// (row, chunk); lane k holds tile k of the chunk (the 64 tiles of 128
+// columns that make 8192 entries) and a fixed butterfly merges them, so
+// lane 0's result depends only on the row's tiles.
+__global__ __launch_bounds__(256) void logits_chunk_stats_kernel(const float2* tstats, int tiles_n, int M, int nch,
+                                                                 float2* out) {
+  static_assert(kVocabChunk / kLogitsTileN == kWave, "one tile per lane");
+  const long item = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (item >= static_cast<long>(M) * nch) return;
+  const int lane = threadIdx.x % kWave;
+  const int m = static_cast<int>(item / nch), c = static_cast<int>(item % nch);
+  const int k = c * kWave + lane;
+  float mx = -INFINITY, sum = 0.f;
+  if (k < tiles_n) {
+    const float2 t = tstats[static_cast<long>(m) * tiles_n + k];
+    mx = t.x;
+    sum = t.y;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) merge_ms(mx, sum, __shfl_xor(mx, off, kWave), __shfl_xor(sum, off, kWave));
+  if (lane == 0) out[item] = make_float2(mx, sum);
 }
 
 hipError_t launch_gemm(const GemmParams& p, int r, hipStream_t stream) {
@@ -672,6 +760,48 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   p.Nout = Nout;
   p.splits = 1;
   return launch_gemm(p, r, stream) == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+}
+
+size_t isd_lm_head_workspace_size(int M, int V) {
+  if (M < 0 || V < 1) return 0;
+  return (static_cast<size_t>(M) * ((V + kLogitsTileN - 1) / kLogitsTileN) * sizeof(float2) + 255) &
+         ~static_cast<size_t>(255);
+}
+
+int isd_lm_head(const void* h, const void* W, int M, int K, int V, void* logits, int64_t ld, float* chunk_stats,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M < 0 || K < 0 || V < 1 || ld < V) return ISD_E_INVALID;
+  if (M == 0) return ISD_OK;
+  if (!h || !W || !logits || !chunk_stats) return ISD_E_INVALID;
+  if (K == 0 || K % kBK != 0) return ISD_E_UNSUPPORTED;
+  if (!aligned16(h) || !aligned16(W)) return ISD_E_INVALID;
+  if (!ws || ws_bytes < isd_lm_head_workspace_size(M, V) || !aligned16(ws)) return ISD_E_WORKSPACE;
+  const int rc = isd_check_device_internal();
+  if (rc) return rc;
+  GemmParams p{};
+  p.x = static_cast<const uint16_t*>(h);
+  p.w = static_cast<const uint16_t*>(W);
+  p.M = M;
+  p.K = K;
+  p.Nout = V;
+  p.splits = 1;
+  p.yb = static_cast<uint16_t*>(logits);
+  p.ldy = static_cast<long>(ld);
+  p.tstats = static_cast<float2*>(ws);
+  p.tiles_n = (V + kLogitsTileN - 1) / kLogitsTileN;
+  // the two tiles with 128 columns, by the same busiest-CU rule as the projections
+  const long cus = isd_device_cus_internal();
+  auto cost = [&](int tm) {
+    const long wgs = static_cast<long>((M + 64 * tm - 1) / (64 * tm)) * p.tiles_n;
+    return (wgs + cus - 1) / cus * (64 * tm + kLogitsTileN);
+  };
+  hipError_t e = cost(2) <= cost(1) ? launch_tile<2, 2, 4, 0, true>(p, stream) : launch_tile<1, 2, 4, 0, true>(p, stream);
+  if (e != hipSuccess) return ISD_E_LAUNCH;
+  const int nch = (V + kVocabChunk - 1) / kVocabChunk;
+  const long n = static_cast<long>(M) * nch;  // one wave each, four per workgroup
+  hipLaunchKernelGGL(logits_chunk_stats_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const float2*>(ws), p.tiles_n, M, nch, reinterpret_cast<float2*>(chunk_stats));
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
 }  // extern "C"

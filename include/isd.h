@@ -16,6 +16,7 @@
  *   isd_linear        y = x W^T (bf16 in, fp32 out), the base projection
  *   gated_lora_apply  y += s (x A^T) B^T on MASK rows only (R-ISD)
  *   isd_linear_gated  both of the above in one pass
+ *   isd_lm_head       logits = h W^T (bf16) with their softmax chunk statistics
  *
  * Conventions shared by every call:
  *   - Every pointer argument is device memory owned by the caller, except
@@ -231,6 +232,9 @@ typedef struct isd_accept_args {
                          from this device word and `step` is ignored, so one
                          captured HIP graph can be replayed step after step
                          (the caller advances the word between replays) */
+  const float* chunk_stats; /* optional [C][rows][ceil(V/8192)][2]: the chunk
+                         statistics of `logits` as isd_lm_head writes them;
+                         when not NULL the statistics pass is skipped */
 } isd_accept_args;
 
 size_t isd_accept_workspace_size(int C, int N, int V, int rows);
@@ -298,6 +302,36 @@ int isd_linear_gated(const void* x, const void* W, const void* A,
                      const void* B, const uint8_t* is_mask, int M, int K,
                      int Nout, int r, float scale, float* y, void* ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ LM head
+ * The distributions the accept step compares are the softmax of the
+ * logits the model emits at each row of the block (I-DLM page,
+ * "Methodologie d'I-DLM > Entrainement a la coherence introspective": row i
+ * gives the distribution of the token at position i + 1; "Documentation et
+ * ressources > Inference & ISD": p at clean rows, q at MASK rows). The
+ * softmax normaliser of a row is a sum over its vocabulary, so it can be
+ * gathered per chunk while the logits are produced, instead of in a second
+ * pass over them.
+ *
+ * isd_lm_head: logits[M][ld] (bf16 bits) = h[M][K] W[V][K]^T, each value
+ * the fp32 dot product rounded to nearest even, with the same K-order,
+ * M-independent reduction as isd_linear; and chunk_stats[M][nch][2] (fp32,
+ * nch = ceil(V / 8192)): for each row and each run of 8192 vocabulary
+ * entries, (max, sum of exp(l - max)) of the stored bf16 logits - the
+ * statistics isd_accept computes in its first pass. Called with M = C*rows
+ * rows in [C][rows] order on a step's block, its outputs feed isd_accept
+ * through isd_accept_args.logits and .chunk_stats.
+ * ws: isd_lm_head_workspace_size(M, V) bytes, 16-byte aligned, caller-owned,
+ * contents on entry ignored (per-row statistics of 128-column tiles).
+ * h and W 16-byte aligned, row-major, contiguous; ld >= V.
+ * Supported: K multiple of 64. M == 0 returns ISD_OK with nothing launched.
+ * Errors: ISD_E_INVALID (null or misaligned pointer, V < 1, ld < V),
+ * ISD_E_UNSUPPORTED (K), ISD_E_WORKSPACE; nothing is launched on an error.
+ */
+size_t isd_lm_head_workspace_size(int M, int V);
+int isd_lm_head(const void* h, const void* W, int M, int K, int V,
+                void* logits, int64_t ld, float* chunk_stats, void* ws,
+                size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }
