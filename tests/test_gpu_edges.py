@@ -75,6 +75,32 @@ def test_kv_write_partial_rows_and_offsets():
                 assert (kd[p, :, :, s, :] == 7.0).all() and (vd[p, :, s // 8, :, s % 8] == -3.0).all()
 
 
+def test_kv_write_negative_start_writes_the_valid_rows():
+    """A block that starts at position -2 flags ISD_DEV_STATE for its first
+    two rows and writes the others at positions 0, 1, 2; nothing else moves."""
+    Hkv, D, rows = 2, 64, 5
+    case = workload.AttentionCase(66, C=1, rows=rows, Hq=2, Hkv=Hkv, D=D, ctx=[0], headroom=16)
+    kv = dvd.KVCache(case.num_pages, Hkv, D, torch.bfloat16, torch.from_numpy(case.table), DEV)
+    kv.k_pages.fill_(7.0)
+    kv.v_pages.fill_(-3.0)
+    k = workload.normal((1, rows, Hkv, D), 1.0, torch.bfloat16, "cpu", 66, "nk")
+    v = workload.normal((1, rows, Hkv, D), 1.0, torch.bfloat16, "cpu", 66, "nv")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dvd.isd_kv_write(kv, k.to(DEV), v.to(DEV), torch.tensor([-2], dtype=torch.int32, device=DEV), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & dvd.DEV_STATE
+    P = case.num_pages
+    kd = to64(kv.k_pages).reshape(P, Hkv, D // 8, 16, 8)
+    vd = to64(kv.v_pages).reshape(P, Hkv, 2, D, 8)
+    p0 = case.table[0, 0]
+    for t in range(16):
+        if t < 3:
+            assert np.array_equal(kd[p0, :, :, t, :].reshape(Hkv, D), to64(k[0, t + 2]))
+            assert np.array_equal(vd[p0, :, t // 8, :, t % 8], to64(v[0, t + 2]))
+        else:
+            assert (kd[p0, :, :, t, :] == 7.0).all() and (vd[p0, :, t // 8, :, t % 8] == -3.0).all()
+
+
 def test_accept_largest_vocabulary():
     """V = 524,288 (the largest the chunk-statistics cache takes), bf16."""
     t, _ = run_trajectory(3, seed=63, C=2, N=2, V=524288, sigma_l=3.0, sigma_q=0.3,
