@@ -148,23 +148,26 @@ def build(cfg, steps_total, dev):
     # change the work; every layer still lives in its own HBM pages)
     per_pool = num_pages * Hkv * D * 16
     src = workload.normal((per_pool,), 1.0, torch.bfloat16, dev, seed, "kv-src")
-    kvs = []
-    for _ in range(L):
-        kv = dvd.KVCache(num_pages, Hkv, D, torch.bfloat16, table_t, dev)
+    # one allocation for all layers (shared block table), so a step's KV
+    # commit is one isd_kv_write_layers launch
+    kvs, layer_stride = dvd.KVCache.stacked(L, num_pages, Hkv, D, torch.bfloat16, table_t, dev)
+    for kv in kvs:
         kv.k_pages.copy_(src)
         kv.v_pages.copy_(src.flip(0))
-        kvs.append(kv)
     del src
 
     M, H, r = C * R, cfg["hidden"], cfg["lora_rank"]
     HD = Hq * D  # attention output width, the O projection's input
     mask = torch.from_numpy(workload.stride_mask(M, N).astype(np.uint8)).to(dev)
+    # the block's K/V rows of every layer, stacked for the commit
+    k_all = torch.stack([workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "kb", l) for l in range(L)])
+    v_all = torch.stack([workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "vb", l) for l in range(L)])
     layers = []
     for l in range(L):
         lay = dict(
             q=workload.normal((C, R, Hq, D), 1.0, torch.bfloat16, dev, seed, "q", l),
-            k=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "kb", l),
-            v=workload.normal((C, R, Hkv, D), 1.0, torch.bfloat16, dev, seed, "vb", l),
+            k=k_all[l],
+            v=v_all[l],
             x=workload.normal((M, H), 1.0, torch.bfloat16, dev, seed, "x", l),
             xo=workload.normal((M, HD), 1.0, torch.bfloat16, dev, seed, "xo", l),
             out=torch.empty((C, R, Hq, D), dtype=torch.float32, device=dev),
@@ -194,7 +197,8 @@ def build(cfg, steps_total, dev):
         lay["proj"] = proj
         layers.append(lay)
     lora_ws = torch.empty(dvd.isd_lora_workspace_size(M, 3 * r), dtype=torch.uint8, device=dev)
-    return dict(ctx0=ctx0, kvs=kvs, layers=layers, mask=mask, lora_ws=lora_ws, table=table)
+    return dict(ctx0=ctx0, kvs=kvs, layer_stride=layer_stride, k_all=k_all, v_all=v_all, layers=layers, mask=mask,
+                lora_ws=lora_ws, table=table)
 
 
 def dry_run(cfg, steps_total, ctx0, dev):
@@ -387,6 +391,10 @@ def main():
     ap.add_argument("--N", type=int, default=4, help="stride N (2N-row blocks); default 4")
     ap.add_argument("--accept", type=float, default=0.9, choices=(0.5, 0.7, 0.9),
                     help="mean per-draft acceptance the draft noise is set for; default 0.9")
+    ap.add_argument("--kv", choices=("commit", "write"), default="commit",
+                    help="commit (default): attention reads the block's own K/V from its rows and one "
+                         "isd_kv_write_layers after the accept writes the accepted rows of every layer; write: "
+                         "isd_kv_write of the whole block before each attention call")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip the LM-head leg (isd_lm_head timed after the steps; not part of the step)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -422,6 +430,7 @@ def main():
 
     cfg = dict(CFG if args.workload == "8b" else CFG_32B, proposal=args.proposal, lora=args.lora, N=args.N,
                accept=args.accept)
+    commit_mode = args.kv == "commit"
     default_workload = args.workload == "8b" and args.N == 4
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -454,13 +463,19 @@ def main():
                               else dvd.prepare_linear(x, p[name]["W"], p[name]["y"]))
         layer_calls.append(dict(
             qkv=[lg("qkv", lay["x"])],
-            kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
+            kvw=None if commit_mode else dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
             att=dvd.prepare_attention(kv, lay["q"], ctx, max_len, lay["out"], ws=att_ws, slices=args.slices,
-                                      dev_err=err),
+                                      dev_err=err, k_blk=lay["k"] if commit_mode else None,
+                                      v_blk=lay["v"] if commit_mode else None),
             o=lg("o", lay["xo"])))
     s_a, s_b = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
     acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
     acc_out = dvd.AcceptOutputs(C, N, R, dev, diag=False)
+    # commit mode: the contexts before the accept advances them are the
+    # positions of the rows to commit, kv_commit their count
+    ctx_prev = torch.empty_like(ctx)
+    commit = (dvd.prepare_kv_write_layers(st["kvs"][0], st["layer_stride"], st["k_all"], st["v_all"], ctx_prev,
+                                          acc_out.kv_commit, dev_err=err) if commit_mode else None)
 
     # every call runs on torch's current stream, so torch's events bracket
     # exactly the launches of that call. Events go on every PROBE_EVERY-th
@@ -471,6 +486,7 @@ def main():
     att_ev = [[(ev(), ev()) for _ in range(L)] for _ in probes]
     proj_ev = [[(ev(), ev(), ev()) for _ in range(L)] for _ in probes]
     acc_ev = [(ev(), ev()) for _ in probes]
+    com_ev = [ev() for _ in probes]  # end of the KV commit (after the accept's end event)
 
     # --graph: the whole step on one side stream, the logits of step t copied
     # by the device (index from a step word in HBM) into one of two fixed
@@ -492,10 +508,14 @@ def main():
                                       if args.lora == "gated" else dvd.prepare_linear(x, p[name]["W"], p[name]["y"]))
                 layer_calls.append(dict(
                     qkv=[lg("qkv", lay["x"])],
-                    kvw=dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
+                    kvw=None if commit_mode else dvd.prepare_kv_write(kv, lay["k"], lay["v"], ctx, dev_err=err),
                     att=dvd.prepare_attention(kv, lay["q"], ctx, max_len, lay["out"], ws=att_ws,
-                                              slices=args.slices, dev_err=err),
+                                              slices=args.slices, dev_err=err, k_blk=lay["k"] if commit_mode else None,
+                                              v_blk=lay["v"] if commit_mode else None),
                     o=lg("o", lay["xo"])))
+            if commit_mode:
+                commit = dvd.prepare_kv_write_layers(st["kvs"][0], st["layer_stride"], st["k_all"], st["v_all"],
+                                                     ctx_prev, acc_out.kv_commit, dev_err=err)
 
     def step(t, timed_idx=None):
         if args.graph:
@@ -514,7 +534,8 @@ def main():
                 f()
             if timed_idx is not None:
                 proj_ev[timed_idx][l][1].record()
-            c["kvw"]()
+            if c["kvw"] is not None:
+                c["kvw"]()
             if timed_idx is not None:
                 att_ev[timed_idx][l][0].record()
             c["att"]()
@@ -524,12 +545,18 @@ def main():
             if timed_idx is not None:
                 proj_ev[timed_idx][l][2].record()
         s_in, s_out = (s_a, s_b) if t % 2 == 0 else (s_b, s_a)
+        if commit is not None:
+            ctx_prev.copy_(ctx)
         if timed_idx is not None:
             acc_ev[timed_idx][0].record()
         dvd.isd_accept(logits[t], logits[t - 1] if t else None, s_in, s_out, N, cfg["seed"], t, out=acc_out,
                        ws=acc_ws, ctx=ctx, dev_err=err, proposal=cfg["proposal"])
         if timed_idx is not None:
             acc_ev[timed_idx][1].record()
+        if commit is not None:
+            commit()
+            if timed_idx is not None:
+                com_ev[timed_idx].record()
 
     def graph_body(par, timed_idx=None):
         torch.index_select(all_lg, 0, step_t, out=buf[par].unsqueeze(0))
@@ -541,7 +568,8 @@ def main():
                 f()
             if timed_idx is not None:
                 proj_ev[timed_idx][l][1].record()
-            c["kvw"]()
+            if c["kvw"] is not None:
+                c["kvw"]()
             if timed_idx is not None:
                 att_ev[timed_idx][l][0].record()
             c["att"]()
@@ -551,12 +579,18 @@ def main():
             if timed_idx is not None:
                 proj_ev[timed_idx][l][2].record()
         s_in, s_out = (s_a, s_b) if par == 0 else (s_b, s_a)
+        if commit is not None:
+            ctx_prev.copy_(ctx)
         if timed_idx is not None:
             acc_ev[timed_idx][0].record()
         dvd.isd_accept(buf[par], buf[1 - par], s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws, ctx=ctx,
                        dev_err=err, proposal=cfg["proposal"], step_dev=step_t, stream=gs)
         if timed_idx is not None:
             acc_ev[timed_idx][1].record()
+        if commit is not None:
+            commit()
+            if timed_idx is not None:
+                com_ev[timed_idx].record()
         step_t.add_(1)
 
     if args.graph:
@@ -592,6 +626,7 @@ def main():
     o_ms = np.array([[a_end.elapsed_time(c) for (_, _, c), (_, a_end) in zip(row, arow)]
                      for row, arow in zip(proj_ev, att_ev)])  # attention end -> O projection end
     acc_ms = np.array([a.elapsed_time(b) for a, b in acc_ev])
+    com_ms = np.array([b.elapsed_time(c) for (a, b), c in zip(acc_ev, com_ev)]) if commit is not None else None
     att_bytes = np.array([attention_bytes(ctxs[W + i], cfg) for i in probes])  # per launch, per probed step
     acc_bytes = np.array([accept_bytes(nds[W + i], accs[W + i], cfg) for i in probes])
     att_gbps = float(np.sum(att_bytes * L) / np.sum(att_ms) / 1e6)
@@ -633,11 +668,15 @@ def main():
                                 else "stream-K, %s slices" % (args.slices or "automatic")),
             "projections": ("gated LoRA rank %d on MASK rows" % cfg["lora_rank"] if args.lora == "gated"
                             else "base GEMM only (no LoRA)"),
+            "kv": ("block K/V read from its rows by the attention; accepted rows of all layers written after the "
+                   "accept in one isd_kv_write_layers launch" if commit_mode
+                   else "isd_kv_write of the whole block before each attention call"),
             "launch": ("HIP graph replay per step (every %dth timed step eager, with the event probes)" % PROBE_EVERY
                        if args.graph else "eager"),
         },
         "roofline": {
-            "kernel": "isd_attention (main + LSE merge launches of one call)",
+            "kernel": ("isd_attention_with_block" if commit_mode else "isd_attention")
+                      + " (main + LSE merge launches of one call)",
             "bound": "hbm",
             "achieved": round(att_gbps, 1),
             "peak": HBM_PEAK_GBPS,
@@ -648,6 +687,7 @@ def main():
         "timing_probes": f"HIP events on {len(probes)} of the {K} timed steps (every {PROBE_EVERY}th)",
         "attention_ms_per_launch": round(float(att_ms.mean()), 5),
         "accept_ms_per_step": round(float(acc_ms.mean()), 5),
+        "kv_commit_ms_per_step": round(float(com_ms.mean()), 5) if com_ms is not None else None,
         "accept_gbps": round(acc_gbps, 1),
         "attn_accept_gbps": round(aa_gbps, 1),
         "attn_accept_frac_of_peak": round(aa_gbps / HBM_PEAK_GBPS, 4),

@@ -88,6 +88,14 @@ _SIGNATURES = {
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "isd_attention_with_block": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                ctypes.c_void_p]),
+    "isd_kv_write_layers": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "isd_accept_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "isd_accept": (ctypes.c_int, [ctypes.POINTER(IsdAcceptArgs), ctypes.c_void_p]),
     "isd_block_assemble": (ctypes.c_int, [ctypes.POINTER(IsdSeqState), ctypes.c_void_p, ctypes.c_void_p,
@@ -160,13 +168,29 @@ class KVCache:
     of a page is documented in include/isd.h.
     """
 
-    def __init__(self, num_pages, num_kv_heads, head_dim, dtype, block_table, device="cuda"):
+    def __init__(self, num_pages, num_kv_heads, head_dim, dtype, block_table, device="cuda", pools=None):
         self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
         self.dtype = dtype
         n = num_pages * num_kv_heads * head_dim * PAGE_SIZE
-        self.k_pages = torch.zeros(n, dtype=dtype, device=device)
-        self.v_pages = torch.zeros(n, dtype=dtype, device=device)
+        if pools is None:
+            self.k_pages = torch.zeros(n, dtype=dtype, device=device)
+            self.v_pages = torch.zeros(n, dtype=dtype, device=device)
+        else:  # views into storage the caller owns (see stacked)
+            self.k_pages, self.v_pages = pools
         self.block_table = block_table.to(device=device, dtype=torch.int32).contiguous()
+
+    @classmethod
+    def stacked(cls, layers, num_pages, num_kv_heads, head_dim, dtype, block_table, device="cuda"):
+        """One cache per layer in a single [layers, pool] allocation with a
+        shared block table, for isd_kv_write_layers. Returns (caches,
+        layer_stride in elements)."""
+        n = num_pages * num_kv_heads * head_dim * PAGE_SIZE
+        k_all = torch.zeros((layers, n), dtype=dtype, device=device)
+        v_all = torch.zeros((layers, n), dtype=dtype, device=device)
+        table = block_table.to(device=device, dtype=torch.int32).contiguous()
+        caches = [cls(num_pages, num_kv_heads, head_dim, dtype, table, device, pools=(k_all[l], v_all[l]))
+                  for l in range(layers)]
+        return caches, n
 
     def c_struct(self):
         return IsdKvCache(
@@ -184,6 +208,16 @@ def isd_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
     _check(rc, "isd_kv_write")
 
 
+def isd_kv_write_layers(kv, layer_stride, k, v, pos0, nrows=None, dev_err=None, stream=None):
+    """isd_kv_write for every layer: k, v [layers, C, rows, Hkv, D]; layer l's
+    pools start l * layer_stride elements after kv's (layer 0's)."""
+    layers, C, rows = k.shape[0], k.shape[1], k.shape[2]
+    s = kv.c_struct()
+    rc = lib().isd_kv_write_layers(ctypes.byref(s), layers, int(layer_stride), _p(k), _p(v), _p(pos0), _p(nrows), C,
+                                   rows, _p(dev_err), _stream(stream))
+    _check(rc, "isd_kv_write_layers")
+
+
 def attn_invariant(chunk_tiles):
     """`slices` value of the batch-invariant split (ISD_ATTN_INVARIANT)."""
     return -int(chunk_tiles)
@@ -194,8 +228,11 @@ def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, slices=0):
     return int(lib().isd_attention_workspace_size(C, rows, num_q_heads, ctypes.byref(s), max_len, slices))
 
 
-def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, dev_err=None, stream=None):
-    """out [C, rows, Hq, D] fp32 = causal attention of q over the pages."""
+def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, dev_err=None, stream=None,
+                  k_blk=None, v_blk=None):
+    """out [C, rows, Hq, D] fp32 = causal attention of q over the pages; with
+    k_blk, v_blk ([C, rows, Hkv, D]) the block's own keys come from those rows
+    (isd_attention_with_block)."""
     C, rows, Hq, D = q.shape
     if scale is None:
         scale = D ** -0.5
@@ -205,10 +242,16 @@ def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, 
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     s = kv.c_struct()
-    rc = lib().isd_attention(ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
-                             int(slices), _p(out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                             _p(dev_err), _stream(stream))
-    _check(rc, "isd_attention")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if k_blk is None:
+        rc = lib().isd_attention(ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
+                                 int(slices), _p(out), _p(ws), nbytes, _p(dev_err), _stream(stream))
+        _check(rc, "isd_attention")
+    else:
+        rc = lib().isd_attention_with_block(ctypes.byref(s), _p(k_blk), _p(v_blk), _p(q), _p(ctx), C, rows, Hq,
+                                            float(scale), int(max_len), int(slices), _p(out), _p(ws), nbytes,
+                                            _p(dev_err), _stream(stream))
+        _check(rc, "isd_attention_with_block")
     return out
 
 
@@ -408,11 +451,23 @@ def prepare_kv_write(kv, k, v, pos0, nrows=None, dev_err=None, stream=None):
                     _p(dev_err), _stream(stream), keep=(s, kv, k, v, pos0, nrows, dev_err))
 
 
-def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, dev_err=None, stream=None):
+def prepare_kv_write_layers(kv, layer_stride, k, v, pos0, nrows=None, dev_err=None, stream=None):
+    s = kv.c_struct()
+    return Prepared("isd_kv_write_layers", ctypes.byref(s), k.shape[0], int(layer_stride), _p(k), _p(v), _p(pos0),
+                    _p(nrows), k.shape[1], k.shape[2], _p(dev_err), _stream(stream),
+                    keep=(s, kv, k, v, pos0, nrows, dev_err))
+
+
+def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, dev_err=None, stream=None,
+                      k_blk=None, v_blk=None):
     C, rows, Hq, D = q.shape
     scale = D ** -0.5 if scale is None else scale
     s = kv.c_struct()
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if k_blk is not None:
+        return Prepared("isd_attention_with_block", ctypes.byref(s), _p(k_blk), _p(v_blk), _p(q), _p(ctx), C, rows,
+                        Hq, float(scale), int(max_len), int(slices), _p(out), _p(ws), nbytes, _p(dev_err),
+                        _stream(stream), keep=(s, kv, k_blk, v_blk, q, ctx, out, ws, dev_err))
     return Prepared("isd_attention", ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
                     int(slices), _p(out), _p(ws), nbytes, _p(dev_err), _stream(stream),
                     keep=(s, kv, q, ctx, out, ws, dev_err))

@@ -53,6 +53,8 @@ struct AttnParams {
   int CT;            // > 0: batch-invariant split into chunks of CT tiles
   int Kmax;          // chunks per sequence the workspace holds (CT > 0)
   float scale_log2;  // scale * log2(e)
+  const void* k_blk;  // optional [C][rows][Hkv][D]: keys at ctx .. ctx+rows-1 come from
+  const void* v_blk;  // the block's own K/V rows instead of the pages
 };
 
 // K row order inside a 32-key tile: MFMA row i reads tile key pi(i), with
@@ -131,6 +133,38 @@ struct AttnOps<uint16_t> {
       r.v[nb][p] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // K operand from a row-major key vector (a block row): the layout of q.
+  template <int D>
+  static __device__ __forceinline__ void load_k_row(Regs<D>& r, const uint16_t* krow, bool valid, int hh) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) r.k[s] = keep(load16(krow + 16 * s + 8 * hh), valid);
+  }
+  // Keys first_key + j of this lane's run that are block rows (ctx <= key <
+  // limit) take their values from vblk (row 0 at vblk, rows `stride` apart).
+  // Every load is issued (clamped to a valid row) and selected afterwards,
+  // so the 8 * D/32 loads of a lane are in flight together.
+  template <int D>
+  static __device__ __forceinline__ void patch_v(Regs<D>& r, int p, int lane32, int first_key, int ctx, int limit,
+                                                 int rows, const uint16_t* vblk, long stride) {
+    uint16_t val[D / 32][8];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        val[nb][j] = vblk[min(max(first_key + j - ctx, 0), rows - 1) * stride + nb * 32 + lane32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      u32x4 w = __builtin_bit_cast(u32x4, r.v[nb][p]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = first_key + j;
+        const uint32_t mine = (j & 1) ? 0xffff0000u : 0x0000ffffu;  // element j's bits in its word
+        if (key >= ctx && key < limit)
+          w[j >> 1] = (w[j >> 1] & ~mine) | (static_cast<uint32_t>(val[nb][j]) << ((j & 1) * 16));
+      }
+      r.v[nb][p] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
   template <int D>
   static __device__ __forceinline__ f32x16 qk(const Regs<D>& r) {
     f32x16 acc = {};
@@ -204,6 +238,23 @@ struct AttnOps<float> {
       for (int k = 0; k < 8; ++k) {
         bool ok = valid && (first_key + k < limit);
         r.v[nb][8 * p + k] = keep(vpage[(hh * D + nb * 32 + lane32) * 8 + k], ok);
+      }
+  }
+  template <int D>
+  static __device__ __forceinline__ void load_k_row(Regs<D>& r, const float* krow, bool valid, int hh) {
+#pragma unroll
+    for (int s = 0; s < D / 2; ++s) r.k[s] = keep(krow[2 * s + hh], valid);
+  }
+  template <int D>
+  static __device__ __forceinline__ void patch_v(Regs<D>& r, int p, int lane32, int first_key, int ctx, int limit,
+                                                 int rows, const float* vblk, long stride) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = first_key + j;
+        const float val = vblk[min(max(key - ctx, 0), rows - 1) * stride + nb * 32 + lane32];
+        if (key >= ctx && key < limit) r.v[nb][8 * p + j] = val;
       }
   }
   template <int D>
@@ -366,6 +417,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (lt0 >= lt1) continue;
     const int ctx = p.ctx[b];
     const int L = ctx + p.rows;  // positions 0 .. L-1 are read
+    const bool blk = p.k_blk != nullptr;  // keys ctx .. L-1 from the block rows
+    const int page_end = blk ? ctx : L;   // positions read from pages
     const int vis_limit = ctx + irow;
     const int32_t* table = p.block_table + static_cast<size_t>(b) * p.table_stride;
 
@@ -419,7 +472,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     // The piece's page ids are staged in LDS a batch at a time (one
     // cooperative load), so no tile waits on a block-table round trip
     // before it can issue its K/V loads.
-    const int full_end = min(lt1, max(0, min(ctx + 1, p.table_stride * 16) / 32));
+    const int full_end = min(lt1, max(0, min(blk ? ctx : ctx + 1, p.table_stride * 16) / 32));
     for (int bt0 = lt0; bt0 < lt1; bt0 += kTileBatch) {
       const int bt1 = min(lt1, bt0 + kTileBatch);
       __syncthreads();  // the previous batch is no longer read
@@ -480,7 +533,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
           const int first = t0 + 16 * pg;
-          bool valid = first < L;
+          bool valid = first < page_end;
           int pid = 0;
           if (valid) {
             if ((first >> 4) >= p.table_stride) {
@@ -499,10 +552,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           kp[pg] = page_ptr<E, D>(p.k_pages, pid, p.Hkv, g);
           vp[pg] = page_ptr<E, D>(p.v_pages, pid, p.Hkv, g);
         }
-        Ops::template load_k<D>(r, kpg ? kp[1] : kp[0], kpg ? ok[1] : ok[0], kslot, hh);
+        const int kpos = t0 + krow_key;  // this lane's key
+        if (blk && kpos >= ctx) {
+          const E* krow = static_cast<const E*>(p.k_blk) +
+                          ((static_cast<size_t>(b) * p.rows + min(kpos - ctx, p.rows - 1)) * p.Hkv + g) * D;
+          Ops::template load_k_row<D>(r, krow, kpos < L, hh);
+        } else {
+          Ops::template load_k<D>(r, kpg ? kp[1] : kp[0], kpg ? ok[1] : ok[0], kslot, hh);
+        }
 #pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
+        for (int pg = 0; pg < 2; ++pg) {
           Ops::template load_v<D>(r, vp[pg], pg, ok[pg], lane32, hh, t0 + 16 * pg + 8 * hh, L);
+          if (blk)
+            Ops::template patch_v<D>(r, pg, lane32, t0 + 16 * pg + 8 * hh, ctx, L, p.rows,
+                                     static_cast<const E*>(p.v_blk) + (static_cast<size_t>(b) * p.rows * p.Hkv + g) * D,
+                                     static_cast<long>(p.Hkv) * D);
+        }
         consume(Ops::template qk<D>(r), t0, true);
       }
     }
@@ -654,11 +719,17 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(void* k_pages, void* v_pages, const int32_t* block_table,
                                                        int table_stride, int num_pages, int Hkv, const E* k,
                                                        const E* v, const int32_t* pos0, const int32_t* nrows, int C,
-                                                       int rows, int32_t* dev_err) {
+                                                       int rows, int32_t* dev_err, long layer_pool,
+                                                       long layer_rows) {
   constexpr int KP = Elem<E>::kPerVec;
   const int per_row = Hkv * (D / KP);
-  // grid (chunks of one sequence's rows, sequences): b is uniform, so its
-  // position and row count come in through scalar loads
+  // grid (chunks of one sequence's rows, sequences, layers): b is uniform,
+  // so its position and row count come in through scalar loads; layer z
+  // has its pools layer_pool elements and its rows layer_rows elements on
+  k_pages = static_cast<E*>(k_pages) + blockIdx.z * layer_pool;
+  v_pages = static_cast<E*>(v_pages) + blockIdx.z * layer_pool;
+  k += blockIdx.z * layer_rows;
+  v += blockIdx.z * layer_rows;
   const int b = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * per_row) return;
@@ -782,6 +853,44 @@ hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t s
   return hipGetLastError();
 }
 
+// the bodies of isd_attention / isd_attention_with_block and of
+// isd_kv_write / isd_kv_write_layers
+int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk, const void* q, const int32_t* ctx,
+                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, float* out, void* ws,
+                   size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
+
+int kv_write_call(const isd_kv_cache* kv, int layers, int64_t layer_stride, const void* k, const void* v,
+                  const int32_t* pos0, const int32_t* nrows, int C, int rows, int32_t* dev_err, hipStream_t stream) {
+  int rc = check_kv(kv);
+  if (rc) return rc;
+  if (C < 0 || rows < 0) return ISD_E_INVALID;
+  if (C == 0 || rows == 0) return ISD_OK;
+  if (C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
+  if (!k || !v || !pos0) return ISD_E_INVALID;
+  if (!aligned16(k) || !aligned16(v)) return ISD_E_INVALID;
+  rc = isd_check_device_internal();
+  if (rc) return rc;
+  const int D = kv->head_dim;
+  const int KP = kv->dtype == ISD_BF16 ? 8 : 4;
+  const long per_seq = static_cast<long>(rows) * kv->num_kv_heads * (D / KP);
+  const long layer_rows = static_cast<long>(C) * rows * kv->num_kv_heads * D;
+  const dim3 grid(static_cast<unsigned>((per_seq + 255) / 256), static_cast<unsigned>(C), static_cast<unsigned>(layers));
+#define ISD_KVW(E, DD)                                                                                          \
+  hipLaunchKernelGGL((kv_write_kernel<E, DD>), grid, dim3(256), 0, stream, kv->k_pages, kv->v_pages,            \
+                     kv->block_table, kv->table_stride, kv->num_pages, kv->num_kv_heads, static_cast<const E*>(k), \
+                     static_cast<const E*>(v), pos0, nrows, C, rows, dev_err, static_cast<long>(layer_stride),    \
+                     layer_rows)
+  if (kv->dtype == ISD_BF16) {
+    if (D == 128) ISD_KVW(uint16_t, 128);
+    else ISD_KVW(uint16_t, 64);
+  } else {
+    if (D == 128) ISD_KVW(float, 128);
+    else ISD_KVW(float, 64);
+  }
+#undef ISD_KVW
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -797,6 +906,26 @@ size_t isd_attention_workspace_size(int C, int rows, int num_q_heads, const isd_
 int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int C, int rows, int num_q_heads,
                   float scale, int max_len, int slices, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
                   hipStream_t stream) {
+  return attention_call(kv, nullptr, nullptr, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, ws, ws_bytes,
+                        dev_err, stream);
+}
+
+int isd_attention_with_block(const isd_kv_cache* kv, const void* k, const void* v, const void* q,
+                             const int32_t* ctx, int C, int rows, int num_q_heads, float scale, int max_len, int slices,
+                             float* out, void* ws, size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
+  if (!k || !v) return ISD_E_INVALID;
+  if (!aligned16(k) || !aligned16(v)) return ISD_E_INVALID;
+  return attention_call(kv, k, v, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, ws, ws_bytes, dev_err,
+                        stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk, const void* q, const int32_t* ctx,
+                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, float* out, void* ws,
+                   size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
   int rc = check_kv(kv);
   if (rc) return rc;
   if (C == 0) return ISD_OK;
@@ -836,6 +965,8 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   p.CT = plan.CT;
   p.Kmax = plan.Kmax;
   p.scale_log2 = scale * kLog2e;
+  p.k_blk = k_blk;
+  p.v_blk = v_blk;
 
   hipError_t e;
   if (kv->dtype == ISD_BF16)
@@ -847,34 +978,25 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 
+}  // namespace
+
+extern "C" {
+
 int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v, const int32_t* pos0, const int32_t* nrows,
                  int C, int rows, int32_t* dev_err, hipStream_t stream) {
-  int rc = check_kv(kv);
-  if (rc) return rc;
-  if (C < 0 || rows < 0) return ISD_E_INVALID;
-  if (C == 0 || rows == 0) return ISD_OK;
-  if (C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
-  if (!k || !v || !pos0) return ISD_E_INVALID;
-  if (!aligned16(k) || !aligned16(v)) return ISD_E_INVALID;
-  rc = isd_check_device_internal();
-  if (rc) return rc;
-  const int D = kv->head_dim;
-  const int KP = kv->dtype == ISD_BF16 ? 8 : 4;
-  const long per_seq = static_cast<long>(rows) * kv->num_kv_heads * (D / KP);
-  const dim3 grid(static_cast<unsigned>((per_seq + 255) / 256), static_cast<unsigned>(C));
-#define ISD_KVW(E, DD)                                                                                          \
-  hipLaunchKernelGGL((kv_write_kernel<E, DD>), grid, dim3(256), 0, stream, kv->k_pages, kv->v_pages,            \
-                     kv->block_table, kv->table_stride, kv->num_pages, kv->num_kv_heads, static_cast<const E*>(k), \
-                     static_cast<const E*>(v), pos0, nrows, C, rows, dev_err)
-  if (kv->dtype == ISD_BF16) {
-    if (D == 128) ISD_KVW(uint16_t, 128);
-    else ISD_KVW(uint16_t, 64);
-  } else {
-    if (D == 128) ISD_KVW(float, 128);
-    else ISD_KVW(float, 64);
-  }
-#undef ISD_KVW
-  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+  return kv_write_call(kv, 1, 0, k, v, pos0, nrows, C, rows, dev_err, stream);
+}
+
+int isd_kv_write_layers(const isd_kv_cache* kv, int layers, int64_t layer_stride, const void* k, const void* v,
+                        const int32_t* pos0, const int32_t* nrows, int C, int rows, int32_t* dev_err,
+                        hipStream_t stream) {
+  if (layers < 0 || layer_stride < 0) return ISD_E_INVALID;
+  if (layers > 65535) return ISD_E_UNSUPPORTED;  // layers map to a grid dimension
+  if (layers > 1 && layer_stride < static_cast<int64_t>(kv ? kv->num_pages : 0) * (kv ? kv->num_kv_heads : 0) *
+                                        (kv ? kv->head_dim : 0) * 16)
+    return ISD_E_INVALID;  // the layers' pools would overlap
+  if (layers == 0) return check_kv(kv);
+  return kv_write_call(kv, layers, layer_stride, k, v, pos0, nrows, C, rows, dev_err, stream);
 }
 
 }  // extern "C"

@@ -11,6 +11,8 @@
  *
  *   isd_kv_write      put the block's K/V rows into the paged cache
  *   isd_attention     causal GQA attention of the block over the pages
+ *   isd_attention_with_block  the same, the block's own K/V taken from its rows
+ *   isd_kv_write_layers  isd_kv_write for every layer of a model in one launch
  *   isd_accept        vocab softmax, p/q test, residual / bonus draw, proposals
  *   isd_block_assemble  the next step's block: newest token, drafts, MASK
  *   isd_linear        y = x W^T (bf16 in, fp32 out), the base projection
@@ -112,6 +114,22 @@ int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
                  const int32_t* pos0, const int32_t* nrows, int C, int rows,
                  int32_t* dev_err, hipStream_t stream);
 
+/* isd_kv_write_layers: isd_kv_write for `layers` layers that share the
+ * block table and the pool geometry of `kv` (layer 0): layer l's pools start
+ * l * layer_stride elements after kv->k_pages / kv->v_pages (layer_stride >=
+ * the elements of one pool when layers > 1), and its rows l * C * rows * Hkv
+ * * D elements after k / v ([layers][C][rows][Hkv][D]). pos0 and nrows are
+ * shared by all layers. This is the KV commit of a step: after isd_accept,
+ * nrows = kv_commit and pos0 = the contexts before the commit write exactly
+ * the accepted rows of every layer. Errors: as isd_kv_write, and
+ * ISD_E_INVALID for a negative count or overlapping pools,
+ * ISD_E_UNSUPPORTED for more than 65535 layers.
+ */
+int isd_kv_write_layers(const isd_kv_cache* kv, int layers,
+                        int64_t layer_stride, const void* k, const void* v,
+                        const int32_t* pos0, const int32_t* nrows, int C,
+                        int rows, int32_t* dev_err, hipStream_t stream);
+
 /* ------------------------------------------------------- attention
  * Causal grouped-query attention of the stride block over the paged cache
  * (strict causality: I-DLM page, "Methodologie d'I-DLM > Serving compatible
@@ -159,6 +177,24 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx,
                   int C, int rows, int num_q_heads, float scale, int max_len,
                   int slices, float* out, void* ws, size_t ws_bytes,
                   int32_t* dev_err, hipStream_t stream);
+
+/* isd_attention_with_block: isd_attention where keys ctx[b] .. ctx[b] +
+ * rows - 1, the block's own rows, are read from k and v ([C][rows][Hkv][D]
+ * in kv->dtype, 16-byte aligned) instead of the pages, so the pages need to
+ * hold only positions below ctx[b] (and the block table to cover them). The
+ * output equals, bit for bit, isd_kv_write of k and v at ctx followed by
+ * isd_attention; the pages are only read. A step can then attend first and
+ * commit afterwards only the accepted rows (isd_kv_write_layers), with no
+ * write into the pools between the layers' attention calls. Same
+ * arguments, workspace and limits as isd_attention otherwise; ISD_E_INVALID
+ * for a null or misaligned k, v.
+ */
+int isd_attention_with_block(const isd_kv_cache* kv, const void* k,
+                             const void* v, const void* q, const int32_t* ctx,
+                             int C, int rows, int num_q_heads, float scale,
+                             int max_len, int slices, float* out, void* ws,
+                             size_t ws_bytes, int32_t* dev_err,
+                             hipStream_t stream);
 
 /* ---------------------------------------------------------- accept
  * Per-sequence decoding state carried from step to step. Draft j (1-based)

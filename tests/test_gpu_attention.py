@@ -265,3 +265,111 @@ def test_invariant_split_at_the_bench_shape_sampled_rows():
     torch.cuda.synchronize()
     assert err.item() == 0
     assert torch.equal(bits(blk[seqs]), bits(one))
+
+
+def block_rows(case, dev=DEV):
+    """The block's own K/V rows [C, rows, Hkv, D] (positions ctx .. ctx+rows-1)."""
+    k = torch.stack([case.k_rows[b, int(c):int(c) + case.rows] for b, c in enumerate(case.ctx)])
+    v = torch.stack([case.v_rows[b, int(c):int(c) + case.rows] for b, c in enumerate(case.ctx)])
+    return k.to(dev).contiguous(), v.to(dev).contiguous()
+
+
+@pytest.mark.parametrize("slices,dtype", [(0, torch.bfloat16), (5, torch.bfloat16),
+                                          (dvd.attn_invariant(1), torch.bfloat16),
+                                          (dvd.attn_invariant(2), torch.bfloat16), (0, torch.float32)])
+def test_attention_with_block_equals_write_then_attend(slices, dtype):
+    """isd_attention_with_block over pages that hold only the cached context
+    equals isd_kv_write of the block followed by isd_attention, bit for bit,
+    and leaves the pages as they were. Contexts put blocks across page (16),
+    tile (32) and chunk (32t) boundaries, with empty and one-token caches."""
+    D = 128 if dtype == torch.bfloat16 else 64
+    case = workload.AttentionCase(71, C=6, rows=8, Hq=32, Hkv=8, D=D, ctx=[0, 1, 28, 60, 125, 250], dtype=dtype)
+    print(f"attention with block slices={slices} {dtype}", flush=True)
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    zeros = torch.zeros(case.C, dtype=torch.int32, device=DEV)
+    kb, vb = block_rows(case)
+    max_len = int(case.lengths.max())
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv = dvd.KVCache(case.num_pages, case.Hkv, case.D, dtype, torch.from_numpy(case.table), DEV)
+    dvd.isd_kv_write(kv, case.k_rows.to(DEV).contiguous(), case.v_rows.to(DEV).contiguous(), zeros, ctx, dev_err=err)
+    torch.cuda.synchronize()
+    before = kv.k_pages.clone(), kv.v_pages.clone()
+    got = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=max_len, slices=slices, dev_err=err, k_blk=kb, v_blk=vb)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k_pages, before[0]) and torch.equal(kv.v_pages, before[1])
+    dvd.isd_kv_write(kv, kb, vb, ctx, dev_err=err)
+    want = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=max_len, slices=slices, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(got), bits(want))
+    kp, vp = oracle_pages(case)
+    ref_out = ref.block_attention(to64(case.q), kp, vp, case.table, case.ctx)
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert slab_errors(got.cpu().double().numpy(), ref_out).max() < tol
+
+
+def test_attention_with_block_needs_pages_only_below_ctx():
+    """Block-table entries past the cached context are -1 (no page yet): no
+    error is flagged and the output is the oracle's."""
+    case = workload.AttentionCase(73, C=3, rows=8, Hq=8, Hkv=2, D=64, ctx=[16, 40, 100])
+    table = case.table.copy()
+    for b, c in enumerate(case.ctx):
+        table[b, -(-int(c) // 16):] = -1  # pages wholly past the context
+    kv = dvd.KVCache(case.num_pages, case.Hkv, case.D, case.dtype, torch.from_numpy(table), DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    dvd.isd_kv_write(kv, case.k_rows.to(DEV).contiguous(), case.v_rows.to(DEV).contiguous(),
+                     torch.zeros(case.C, dtype=torch.int32, device=DEV), ctx, dev_err=err)
+    kb, vb = block_rows(case)
+    for slices in (0, dvd.attn_invariant(1)):
+        got = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=int(case.lengths.max()), slices=slices,
+                                dev_err=err, k_blk=kb, v_blk=vb)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        kp, vp = oracle_pages(case)
+        want = ref.block_attention(to64(case.q), kp, vp, case.table, case.ctx)
+        assert slab_errors(got.cpu().double().numpy(), want).max() < 2e-3
+
+
+def test_attention_with_block_rows_equal_one_row_calls():
+    """Lossless R-ISD with the block read from its rows: row i of a block
+    call equals the one-row call at ctx + i (earlier rows already in the
+    pages, its own row from the block), bit for bit, in the invariant split."""
+    t, C, rows, Hq, D = 2, 5, 8, 32, 128
+    case = workload.AttentionCase(74, C=C, rows=rows, Hq=Hq, Hkv=8, D=D, ctx=[0, 30, 61, 64, 200])
+    kv, err = fill_cache(case)  # every position, so the one-row calls find rows < ctx + i in the pages
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    kb, vb = block_rows(case)
+    inv = dvd.attn_invariant(t)
+    max_len = int(case.lengths.max())
+    blk = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=max_len, slices=inv, dev_err=err, k_blk=kb, v_blk=vb)
+    ar = copy.copy(kv)
+    ar.block_table = kv.block_table.repeat_interleave(rows, dim=0).contiguous()
+    ctx1 = (ctx[:, None] + torch.arange(rows, device=DEV, dtype=torch.int32)[None, :]).reshape(-1).contiguous()
+    q1 = case.q.to(DEV).reshape(C * rows, 1, Hq, D).contiguous()
+    one = dvd.isd_attention(ar, q1, ctx1, max_len=max_len, slices=inv, dev_err=err,
+                            k_blk=kb.reshape(C * rows, 1, 8, D).contiguous(), v_blk=vb.reshape(C * rows, 1, 8, D).contiguous())
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(blk), bits(one))
+
+
+def test_kv_write_layers_equals_per_layer_calls():
+    """Three layers in one stacked allocation, committed in one launch with
+    per-sequence start and row counts, equal three isd_kv_write calls."""
+    L, C, rows, Hkv, D = 3, 4, 8, 8, 128
+    case = workload.AttentionCase(75, C=C, rows=rows, Hq=8, Hkv=Hkv, D=D, ctx=[3, 17, 40, 64], headroom=8)
+    caches, stride = dvd.KVCache.stacked(L, case.num_pages, Hkv, D, torch.bfloat16, torch.from_numpy(case.table), DEV)
+    k = workload.normal((L, C, rows, Hkv, D), 1.0, torch.bfloat16, "cpu", 75, "lk").to(DEV)
+    v = workload.normal((L, C, rows, Hkv, D), 1.0, torch.bfloat16, "cpu", 75, "lv").to(DEV)
+    pos0 = torch.from_numpy(case.ctx).to(DEV)
+    nrows = torch.tensor([8, 3, 1, 0], dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dvd.isd_kv_write_layers(caches[0], stride, k, v, pos0, nrows, dev_err=err)
+    for l in range(L):
+        ref_kv = dvd.KVCache(case.num_pages, Hkv, D, torch.bfloat16, torch.from_numpy(case.table), DEV)
+        dvd.isd_kv_write(ref_kv, k[l].contiguous(), v[l].contiguous(), pos0, nrows, dev_err=err)
+        torch.cuda.synchronize()
+        assert torch.equal(caches[l].k_pages.view(torch.int16), ref_kv.k_pages.view(torch.int16))
+        assert torch.equal(caches[l].v_pages.view(torch.int16), ref_kv.v_pages.view(torch.int16))
+    assert err.item() == 0
