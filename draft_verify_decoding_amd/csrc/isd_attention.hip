@@ -23,10 +23,15 @@
 //  * Page layout (isd.h) makes every operand a run of 16 contiguous bytes
 //    and every 4-lane group a run of 64: K [Hkv][D/8][16 slots][8],
 //    V [Hkv][2 half-pages][D][8 slots].
-//  * Split-KV: a workgroup of 4 waves reduces one chunk of one (sequence,
-//    KV head); waves interleave 32-key tiles and merge through LDS; units
-//    with several chunks write (m, l, O) partials that a second kernel merges
-//    in chunk order, so results do not depend on scheduling.
+//  * Split-KV: a workgroup holds one wave per (KV head, query block) of a
+//    head group; its waves walk the same 32-key tiles (all heads of a page
+//    are contiguous). Its share of keys is an equal run of the tiles of all
+//    sequences (stream-K) or one fixed-size chunk of one sequence (the
+//    batch-invariant split); a sequence cut into several shares leaves
+//    (m, l, O) partials that a second kernel merges in share order, so
+//    results do not depend on scheduling.
+//  * The block's own K/V may come from its rows instead of the pages
+//    (isd_attention_with_block): only the boundary tiles read them.
 #include "isd_common.hpp"
 
 #include <algorithm>

@@ -11,11 +11,13 @@
 // operands K-contiguous). Four waves in a 2 x 2 grid, each TM x TN blocks of
 // 32 x 32 (v_mfma_f32_32x32x16_bf16). K advances in slabs of 64 that travel
 // from global memory straight into LDS (16-byte direct loads, XOR-swizzled
-// rows, no register staging), three or four stages deep with one barrier per
+// rows, no register staging), three to five stages deep with one barrier per
 // slab. The per-output reduction order is slab by slab in ascending K and
 // does not depend on M, the tile choice, the other rows or the mask. A
 // split-K launch runs the same loop over a fixed share of the slabs (the
 // split count depends only on K).
+// LM head: the same loop with an epilogue that stores bf16 logits and the
+// per-row softmax statistics of each 128-column tile (isd_lm_head).
 // LoRA: U = x A^T first, as a split-K GEMM whose partials are summed in
 // split order. The delta U B^T of a 32x32 output block then runs on bf16
 // MFMA with U split into bf16 high and low halves (about 16 mantissa bits):
