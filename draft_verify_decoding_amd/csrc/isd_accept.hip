@@ -24,8 +24,8 @@
 //           sequence, zeroed by the stats launch) then picks and rescans the
 //           residual chunk and writes the outputs and the next state.
 // When the caller passes the chunk statistics (isd_lm_head wrote them with
-// the logits), a one-block launch that zeroes the counters replaces the
-// stats launch.
+// the logits), a small launch that zeroes the counters replaces the stats
+// launch.
 #include "isd_common.hpp"
 
 namespace isd {
