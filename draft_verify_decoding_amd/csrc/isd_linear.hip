@@ -128,6 +128,7 @@ struct GemmParams {
   long ldy;
   float2* tstats;       // [M][tiles_n] (max, sum exp(l - max)) of the tile's columns
   int tiles_n;
+  int yb_vec;           // rows of yb start 16-byte aligned: store them 16 bytes at a time
 };
 
 // Wait until at most n vector-memory operations of this wave are in flight
@@ -346,59 +347,59 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   wait_vm_lgkm0<0>();
 
   // LM head: the logits are rounded to bf16 (the values the accept step
-  // reads) and stored; per row, the (max, sum of exp(l - max)) of the
-  // tile's BN columns follows from those rounded values. Register e of lane
-  // (j, hh) is row 8(e/4) + 4hh + e%4 of the 32x32 block, column j: a
-  // butterfly over the 32 lanes of a half gives every lane the row's value
-  // (the pairs add the same two numbers, so all lanes agree), the TN blocks
-  // of a wave are combined first, and the two waves that share rows are
-  // merged through LDS, the left one first. Columns past Nout count as -inf.
+  // reads) and parked in LDS as the tile's [BM][BN] rows. Each thread then
+  // takes 8 consecutive columns of a row: it stores them with one 16-byte
+  // store (whole cache lines per row), and the 16 threads of a row form the
+  // row's (max, sum of exp(l - max)) over the tile's 128 columns with a
+  // fixed 4-step butterfly. Columns past Nout count as -inf.
   if constexpr (kLogits) {
     static_assert(R16 == 0, "the logits epilogue has no adapter");
-    float2* sms = reinterpret_cast<float2*>(stage_ptr(0));  // [BM][2]
-    static_assert(BM * 2 * 8 <= STAGE * 2, "row partials fit one stage");
+    static_assert(BN == 128 && BM * BN <= STAGE, "a 128-column tile fits one stage");
+    uint16_t* tileb = stage_ptr(0);  // [BM][BN]
     stage_barrier();  // every wave is done with the stages
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m0 = m_blk + wm + 32 * i;
-      float xv[TN][16];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n_blk + wn + 32 * j + lane32;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const uint32_t bits = f32_to_bf16_bits(acc[i][j][e]);
-          if (row < p.M && col < p.Nout) p.yb[static_cast<long>(row) * p.ldy + col] = static_cast<uint16_t>(bits);
-          xv[j][e] = col < p.Nout ? bf16_bits_to_f32(static_cast<uint16_t>(bits)) : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float m = xv[0][e];
-#pragma unroll
-        for (int j = 1; j < TN; ++j) m = fmaxf(m, xv[j][e]);
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
-        float sum = 0.f;
-        if (m != -INFINITY) {
-          const float ml = m * kLog2e;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) sum += weight_of(xv[j][e], ml);
-        }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) sum += shfl_xor_f(sum, off);
-        if (lane32 == 0) sms[(wm + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * 2 + (wn != 0)] = make_float2(m, sum);
-      }
-    }
+        for (int e = 0; e < 16; ++e)
+          tileb[(wm + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * BN + wn + 32 * j + lane32] =
+              static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][e]));
     wait_vm_lgkm0<0>();
     stage_barrier();
-    for (int r = tid; r < BM; r += 256) {
-      const int row = m_blk + r;
-      if (row >= p.M) break;
-      float m = sms[2 * r].x, sum = sms[2 * r].y;
-      merge_ms(m, sum, sms[2 * r + 1].x, sms[2 * r + 1].y);
-      p.tstats[static_cast<long>(row) * p.tiles_n + n_blk / BN] = make_float2(m, sum);
+    for (int idx = tid; idx < BM * (BN / 8); idx += 256) {  // 16 threads (lanes 16q .. 16q+15) per row
+      const int r = idx / (BN / 8), c = 8 * (idx % (BN / 8));
+      const int row = m_blk + r, col = n_blk + c;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tileb + r * BN + c);
+      if (row < p.M) {
+        uint16_t* dst = p.yb + static_cast<long>(row) * p.ldy + col;
+        if (p.yb_vec && col + 8 <= p.Nout) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const uint16_t* ev = reinterpret_cast<const uint16_t*>(&v);
+          for (int k = 0; k < 8; ++k)
+            if (col + k < p.Nout) dst[k] = ev[k];
+        }
+      }
+      float x[8];
+      unpack16(v, x);
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[k] = col + k < p.Nout ? x[k] : -INFINITY;
+        m = fmaxf(m, x[k]);
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+      float sum = 0.f;
+      if (m != -INFINITY) {
+        const float ml = m * kLog2e;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum += weight_of(x[k], ml);
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) sum += shfl_xor_f(sum, off);
+      if (c == 0 && row < p.M) p.tstats[static_cast<long>(row) * p.tiles_n + n_blk / BN] = make_float2(m, sum);
     }
     return;
   }
@@ -791,6 +792,7 @@ int isd_lm_head(const void* h, const void* W, int M, int K, int V, void* logits,
   p.ldy = static_cast<long>(ld);
   p.tstats = static_cast<float2*>(ws);
   p.tiles_n = (V + kLogitsTileN - 1) / kLogitsTileN;
+  p.yb_vec = ld % 8 == 0 && aligned16(logits);
   // the two tiles with 128 columns, by the same busiest-CU rule as the projections
   const long cus = isd_device_cus_internal();
   auto cost = [&](int tm) {
