@@ -373,3 +373,33 @@ def test_kv_write_layers_equals_per_layer_calls():
         assert torch.equal(caches[l].k_pages.view(torch.int16), ref_kv.k_pages.view(torch.int16))
         assert torch.equal(caches[l].v_pages.view(torch.int16), ref_kv.v_pages.view(torch.int16))
     assert err.item() == 0
+
+
+@pytest.mark.parametrize("shape", ["8b", "32b"])
+def test_timed_launch_configuration_against_the_oracle(shape):
+    """The call the step benchmark times, at its full shapes: the block's K/V
+    read from its rows (pages hold only the cached context), the
+    batch-invariant split with 64-tile chunks (8B: C=64, 32/8 heads, ragged
+    1K-8K contexts) or 66-tile chunks (32B: C=16, 64/8 heads, 16,384
+    cached tokens). The whole batch runs; sampled sequences are checked
+    against the oracle in full."""
+    if shape == "8b":
+        case = workload.AttentionCase(81, C=64, rows=8, Hq=32, Hkv=8, D=128, ctx=("uniform", 1024, 8192))
+        t, seqs = 64, np.array([1, 14, 27, 40, 52, 63])
+    else:
+        case = workload.AttentionCase(82, C=16, rows=8, Hq=64, Hkv=8, D=128, ctx=16384)
+        t, seqs = 66, np.array([0, 11])
+    print(f"timed launch configuration {shape} t={t}", flush=True)
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv = dvd.KVCache(case.num_pages, case.Hkv, case.D, case.dtype, torch.from_numpy(case.table), DEV)
+    dvd.isd_kv_write(kv, case.k_rows.to(DEV).contiguous(), case.v_rows.to(DEV).contiguous(),
+                     torch.zeros(case.C, dtype=torch.int32, device=DEV), ctx, dev_err=err)
+    kb, vb = block_rows(case)
+    got = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=int(case.lengths.max()), slices=dvd.attn_invariant(t),
+                            dev_err=err, k_blk=kb, v_blk=vb)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q)[seqs], kp, vp, case.table[seqs], case.ctx[seqs])
+    assert slab_errors(got.cpu().double().numpy()[seqs], want).max() < 2e-3
