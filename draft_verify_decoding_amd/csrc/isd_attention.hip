@@ -307,6 +307,49 @@ __device__ __forceinline__ const E* page_ptr(const void* pool, int pid, int Hkv,
 // of one column does not depend on the others. So a row of a block of rows
 // comes out bit for bit equal to the same query sent alone with ctx + row
 // cached tokens (the autoregressive forward), whatever else is in the batch.
+// Exclusive prefix sum of count(b) over the C sequences into s_off[0..C]
+// (s_off[C] = total), by all `nthreads` threads of the workgroup: each sums
+// a run of sequences, a scan inside each wave, then the totals of the waves
+// before (integer adds, so the order is free). count is called twice per
+// sequence; `visit(b)` runs once per sequence, on the thread that owns it.
+template <typename Count, typename Visit>
+__device__ __forceinline__ void prefix_over_sequences(int C, int nthreads, int* s_off, int* s_part, Count count,
+                                                      Visit visit) {
+  const int per = (C + nthreads - 1) / nthreads;
+  const int b0 = threadIdx.x * per;
+  int sum = 0;
+  for (int b = b0; b < min(C, b0 + per); ++b) sum += count(b);
+  const int ln = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (ln >= d) incl += v;
+  }
+  if (ln == kWave - 1) s_part[wv] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w2 = 0; w2 < wv; ++w2) run += s_part[w2];
+  for (int b = b0; b < min(C, b0 + per); ++b) {
+    s_off[b] = run;
+    visit(b);
+    run += count(b);
+  }
+  if (b0 < C && min(C, b0 + per) == C) s_off[C] = run;
+  __syncthreads();
+}
+
+// Largest b in [0, C) with s_off[b] <= x (x < s_off[C]): the sequence whose
+// range of the prefix holds x (sequences with an empty range are skipped).
+__device__ __forceinline__ int sequence_holding(const int* s_off, int C, long x) {
+  int lo = 0, hi = C - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (s_off[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <typename E, int D, bool kChunked>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   using Ops = AttnOps<E>;
@@ -316,7 +359,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int w = blockIdx.x % G;
   const int nthreads = 64 * p.HPW * MB;
 
-  // Tile offsets of the sequences (prefix sum, stream-K split only).
+  // Prefix over the sequences: tile offsets (stream-K split) or chunk
+  // offsets (chunked split).
   __shared__ int s_off[kMaxSeqs + 1];
   __shared__ int s_part[512 / kWave];  // per-wave totals of the prefix sum
   __shared__ int s_pid[2 * kTileBatch];  // page ids of the current tile batch
@@ -324,65 +368,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   int u_first = 0;                   // first sequence of this workgroup
   int c_nt = 0, c_units = 0, c_k = 0;  // chunked split: tiles, chunks, this chunk
   if constexpr (kChunked) {
-    // workgroup w of a head group owns chunk w % Kmax of sequence w / Kmax;
-    // workgroups past the sequence's last chunk leave at once
-    u_first = w / p.Kmax;
-    c_k = w % p.Kmax;
-    const int ctx = p.ctx[u_first];
-    const bool reporter = c_k == 0 && hg == 0 && threadIdx.x == 0;
-    if (ctx < 0) {
-      if (reporter) set_dev_err(p.dev_err, ISD_DEV_STATE);
-      return;
-    }
-    c_nt = (ctx + p.rows + 31) / 32;
+    // The chunks of all sequences, in sequence order, go to consecutive
+    // workgroups of the head group (workgroup w takes the w-th); the
+    // workgroups past the last chunk leave at once. Consecutive ids are
+    // spread over the XCDs in turn, so every XCD gets an equal count of
+    // chunks, and as long as there are no more chunks than CUs they all run
+    // in one round. A sequence flagged bad (ctx < 0, or ctx + rows beyond the
+    // chunks the workspace holds) has no chunks.
+    auto units_of = [&](int b) {
+      const int ctx = p.ctx[b];
+      if (ctx < 0) return 0;
+      const int u = ((ctx + p.rows + 31) / 32 + p.CT - 1) / p.CT;
+      return u > p.Kmax ? 0 : u;
+    };
+    prefix_over_sequences(p.C, nthreads, s_off, s_part, units_of, [&](int b) {
+      if (w != 0 || hg != 0) return;
+      const int ctx = p.ctx[b];
+      if (ctx < 0) set_dev_err(p.dev_err, ISD_DEV_STATE);
+      else if (((ctx + p.rows + 31) / 32 + p.CT - 1) / p.CT > p.Kmax) set_dev_err(p.dev_err, ISD_DEV_CAPACITY);
+    });
+    if (w >= s_off[p.C]) return;
+    u_first = sequence_holding(s_off, p.C, w);
+    c_k = w - s_off[u_first];
+    c_nt = (p.ctx[u_first] + p.rows + 31) / 32;
     c_units = (c_nt + p.CT - 1) / p.CT;
-    if (c_units > p.Kmax) {  // ctx + rows beyond max_len: no room for its chunks
-      if (reporter) set_dev_err(p.dev_err, ISD_DEV_CAPACITY);
-      return;
-    }
-    if (c_k >= c_units) return;
   } else {
-    const int per = (p.C + nthreads - 1) / nthreads;
-    const int b0 = threadIdx.x * per;
-    int sum = 0;
-    for (int b = b0; b < min(p.C, b0 + per); ++b) {
-      const int ctx = p.ctx[b];
-      sum += ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
-    }
-    // exclusive prefix over the threads: a scan inside each wave, then the
-    // totals of the waves before (integer adds, so the order is free)
-    const int ln = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    int incl = sum;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (ln >= d) incl += v;
-    }
-    if (ln == kWave - 1) s_part[wv] = incl;
-    __syncthreads();
-    int run = incl - sum;
-    for (int w2 = 0; w2 < wv; ++w2) run += s_part[w2];
-    for (int b = b0; b < min(p.C, b0 + per); ++b) {
-      s_off[b] = run;
-      const int ctx = p.ctx[b];
-      if (ctx < 0 && w == 0 && hg == 0) set_dev_err(p.dev_err, ISD_DEV_STATE);
-      run += ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
-    }
-    if (b0 < p.C && min(p.C, b0 + per) == p.C) s_off[p.C] = run;
-    __syncthreads();
+    prefix_over_sequences(
+        p.C, nthreads, s_off, s_part,
+        [&](int b) {
+          const int ctx = p.ctx[b];
+          return ctx < 0 ? 0 : (ctx + p.rows + 31) / 32;
+        },
+        [&](int b) {
+          if (p.ctx[b] < 0 && w == 0 && hg == 0) set_dev_err(p.dev_err, ISD_DEV_STATE);
+        });
     const long T = s_off[p.C];
     t_begin = static_cast<int>(w * T / G);
     t_end = static_cast<int>((w + 1) * T / G);
     if (w == 0 && hg == 0)  // the merge launch reads the offsets back
       for (int b = threadIdx.x; b <= p.C; b += nthreads) p.tile_off[b] = s_off[b];
     if (t_begin >= t_end) return;
-    // sequence holding tile t_begin
-    int lo = 0, hi = p.C - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) / 2;
-      if (s_off[mid] <= t_begin) lo = mid; else hi = mid - 1;
-    }
-    u_first = lo;
+    u_first = sequence_holding(s_off, p.C, t_begin);
   }
 
   const int wave = threadIdx.x / kWave;
