@@ -347,15 +347,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   wait_vm_lgkm0<0>();
 
   // LM head: the logits are rounded to bf16 (the values the accept step
-  // reads) and parked in LDS as the tile's [BM][BN] rows. Each thread then
+  // reads) and parked in LDS as the tile's [BM][BN] rows (in stage 0, and
+  // in stage 1 for the rows that do not fit a stage). Each thread then
   // takes 8 consecutive columns of a row: it stores them with one 16-byte
   // store (whole cache lines per row), and the 16 threads of a row form the
   // row's (max, sum of exp(l - max)) over the tile's 128 columns with a
   // fixed 4-step butterfly. Columns past Nout count as -inf.
   if constexpr (kLogits) {
     static_assert(R16 == 0, "the logits epilogue has no adapter");
-    static_assert(BN == 128 && BM * BN <= STAGE, "a 128-column tile fits one stage");
-    uint16_t* tileb = stage_ptr(0);  // [BM][BN]
+    constexpr int kRowsPerStage = STAGE / BN;
+    static_assert(BN == 128 && BM <= 2 * kRowsPerStage, "a 128-column tile fits two stages");
+    uint16_t* const tile0 = stage_ptr(0);
+    uint16_t* const tile1 = stage_ptr(1);
+    auto tile_row = [&](int r) { return r < kRowsPerStage ? tile0 + r * BN : tile1 + (r - kRowsPerStage) * BN; };
     stage_barrier();  // every wave is done with the stages
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -363,14 +367,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          tileb[(wm + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3)) * BN + wn + 32 * j + lane32] =
+          tile_row(wm + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3))[wn + 32 * j + lane32] =
               static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][e]));
     wait_vm_lgkm0<0>();
     stage_barrier();
     for (int idx = tid; idx < BM * (BN / 8); idx += 256) {  // 16 threads (lanes 16q .. 16q+15) per row
       const int r = idx / (BN / 8), c = 8 * (idx % (BN / 8));
       const int row = m_blk + r, col = n_blk + c;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tileb + r * BN + c);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tile_row(r) + c);
       if (row < p.M) {
         uint16_t* dst = p.yb + static_cast<long>(row) * p.ldy + col;
         if (p.yb_vec && col + 8 <= p.Nout) {
@@ -793,13 +797,18 @@ int isd_lm_head(const void* h, const void* W, int M, int K, int V, void* logits,
   p.tstats = static_cast<float2*>(ws);
   p.tiles_n = (V + kLogitsTileN - 1) / kLogitsTileN;
   p.yb_vec = ld % 8 == 0 && aligned16(logits);
-  // the two tiles with 128 columns, by the same busiest-CU rule as the projections
+  // a tile of 128 columns and 256, 128 or 64 rows, by the same busiest-CU
+  // rule as the projections (the earlier, taller tile wins a tie); the
+  // 256-row tile has three stages of 48 KB, the others four of 32 or 24 KB
   const long cus = isd_device_cus_internal();
   auto cost = [&](int tm) {
     const long wgs = static_cast<long>((M + 64 * tm - 1) / (64 * tm)) * p.tiles_n;
     return (wgs + cus - 1) / cus * (64 * tm + kLogitsTileN);
   };
-  hipError_t e = cost(2) <= cost(1) ? launch_tile<2, 2, 4, 0, true>(p, stream) : launch_tile<1, 2, 4, 0, true>(p, stream);
+  const int tm = cost(4) <= cost(2) ? (cost(4) <= cost(1) ? 4 : 1) : (cost(2) <= cost(1) ? 2 : 1);
+  hipError_t e = tm == 4   ? launch_tile<4, 2, 3, 0, true>(p, stream)
+                 : tm == 2 ? launch_tile<2, 2, 4, 0, true>(p, stream)
+                           : launch_tile<1, 2, 4, 0, true>(p, stream);
   if (e != hipSuccess) return ISD_E_LAUNCH;
   const int nch = (V + kVocabChunk - 1) / kVocabChunk;
   const long n = static_cast<long>(M) * nch;  // one wave each, four per workgroup
