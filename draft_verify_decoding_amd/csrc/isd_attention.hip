@@ -307,6 +307,22 @@ __device__ __forceinline__ const E* page_ptr(const void* pool, int pid, int Hkv,
 // of one column does not depend on the others. So a row of a block of rows
 // comes out bit for bit equal to the same query sent alone with ctx + row
 // cached tokens (the autoregressive forward), whatever else is in the batch.
+// Cache-policy operand of a direct-to-LDS load: non-temporal (the K/V
+// stream through once, as the register loads' non-temporal hint says).
+constexpr int kNonTemporal = 2;
+
+// Wait until this wave's vector-memory operations (vm = 0) or its LDS
+// operations (lgkm = 0) are done; the exp counter is not waited on.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier with no memory fence (the waits it needs are explicit);
+// the empty asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Exclusive prefix sum of count(b) over the C sequences into s_off[0..C]
 // (s_off[C] = total), by all `nthreads` threads of the workgroup: each sums
 // a run of sequences, a scan inside each wave, then the totals of the waves
@@ -350,7 +366,7 @@ __device__ __forceinline__ int sequence_holding(const int* s_off, int C, long x)
   return lo;
 }
 
-template <typename E, int D, bool kChunked>
+template <typename E, int D, bool kChunked, bool kShare>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   using Ops = AttnOps<E>;
   const int MB = p.MB;
@@ -364,6 +380,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   __shared__ int s_off[kMaxSeqs + 1];
   __shared__ int s_part[512 / kWave];  // per-wave totals of the prefix sum
   __shared__ int s_pid[2 * kTileBatch];  // page ids of the current tile batch
+  // K/V tile of each KV head shared by its MB > 1 query-block waves (bf16):
+  // D / 8 slots of 1 KB (64 lanes x 16 bytes), K runs first, then the V runs
+  // of the tile's two pages.
+  constexpr int kSlotsK = D / 16, kSlots = D / 8;
+  // (kShare: bf16 with MB > 1, so HPW <= 8 / MB <= 4 heads)
+  static_assert(!kShare || std::is_same<E, uint16_t>::value, "shared tiles are bf16");
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[kShare ? 4 * kSlots * 512 : 8];
   int t_begin = 0, t_end = 0;
   int u_first = 0;                   // first sequence of this workgroup
   int c_nt = 0, c_units = 0, c_k = 0;  // chunked split: tiles, chunks, this chunk
@@ -529,6 +552,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           vpage0 = page_ptr<E, D>(p.v_pages, pid0, p.Hkv, g);
           vpage1 = page_ptr<E, D>(p.v_pages, pid1, p.Hkv, g);
         };
+        if constexpr (kShare) {
+          // The MB waves of a KV head (one per query block) need the same
+          // K/V tile. Each loads every MB-th of its 1 KB slots straight into
+          // LDS; after a barrier all of them read the whole tile from there,
+          // so each K/V byte enters the CU once instead of MB times (a CU
+          // streams unique bytes about 1.4x faster than bytes it fetches
+          // twice). The next tile's loads are issued once every wave has read
+          // this one, one tile ahead of use like the loop below.
+          {
+            uint16_t* const tile = s_tile + hl_w * (kSlots * 512);
+            auto issue = [&](int tl) {
+              pages(tl);
+#pragma unroll
+              for (int i = 0; i < kSlots; ++i) {
+                if (i % MB != rb) continue;  // wave-uniform
+                const uint16_t* src;
+                if (i < kSlotsK) {
+                  src = kpage + ((2 * i + hh) * 16 + kslot) * 8;
+                } else {
+                  const int j = i - kSlotsK, pg = j / (D / 32), nb = j % (D / 32);
+                  src = (pg ? vpage1 : vpage0) + (hh * D + nb * 32 + lane32) * 8;
+                }
+                __builtin_amdgcn_global_load_lds(src, tile + i * 512, 16, 0, kNonTemporal);
+              }
+            };
+            issue(lt);
+            for (;;) {
+              const bool more = lt + 1 < fe;
+              wait_vm0();  // this wave's share of tile lt is in LDS
+              plain_barrier();
+#pragma unroll
+              for (int i = 0; i < kSlots; ++i) {
+                const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + i * 512 + 8 * lane));
+                if (i < kSlotsK) r.k[i] = v;
+                else r.v[(i - kSlotsK) % (D / 32)][(i - kSlotsK) / (D / 32)] = v;
+              }
+              wait_lgkm0();  // every wave holds tile lt in registers before
+              plain_barrier();  // the next tile's loads overwrite it
+              if (more) issue(lt + 1);
+              consume(Ops::template qk<D>(r), 32 * lt, false);
+              ++lt;
+              if (!more) break;
+            }
+          }
+        }
+        if constexpr (!kShare) {
         pages(lt);
         Ops::template load_k<D>(r, kpage, true, kslot, hh);
         Ops::template load_v<D>(r, vpage0, 0, true, lane32, hh, 0, INT_MAX);
@@ -554,6 +623,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           // the barrier count is uniform; it needs no memory fence.
           if ((lt & 3) == 0) __builtin_amdgcn_s_barrier();
           if (!more) break;
+        }
         }
       }
       for (; lt < bt1; ++lt) {  // boundary tiles: causal mask, positions past L, table end
@@ -873,12 +943,16 @@ int plan_attention(int C, int rows, int Hq, const isd_kv_cache* kv, int max_len,
 
 template <typename E, int D>
 hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t stream) {
-  if (p.CT > 0)
-    hipLaunchKernelGGL((attention_kernel<E, D, true>), dim3(static_cast<unsigned>(groups * p.G)),
-                       dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attention_kernel<E, D, false>), dim3(static_cast<unsigned>(groups * p.G)),
-                       dim3(static_cast<unsigned>(64 * p.HPW * p.MB)), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>(groups * p.G)), block(static_cast<unsigned>(64 * p.HPW * p.MB));
+  // bf16 heads with several query-block waves share each K/V tile through LDS
+  const bool share = std::is_same<E, uint16_t>::value && p.MB > 1;
+  if (p.CT > 0) {
+    if (share) hipLaunchKernelGGL((attention_kernel<E, D, true, std::is_same<E, uint16_t>::value>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attention_kernel<E, D, true, false>), grid, block, 0, stream, p);
+  } else {
+    if (share) hipLaunchKernelGGL((attention_kernel<E, D, false, std::is_same<E, uint16_t>::value>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attention_kernel<E, D, false, false>), grid, block, 0, stream, p);
+  }
   hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(p.MB)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
