@@ -821,49 +821,82 @@ __global__ __launch_bounds__(256) void kv_write_kernel(void* k_pages, void* v_pa
                                                        int table_stride, int num_pages, int Hkv, const E* k,
                                                        const E* v, const int32_t* pos0, const int32_t* nrows, int C,
                                                        int rows, int32_t* dev_err, long layer_pool,
-                                                       long layer_rows) {
+                                                       long layer_rows, int k_blocks, int v_units) {
   constexpr int KP = Elem<E>::kPerVec;
-  const int per_row = Hkv * (D / KP);
-  // grid (chunks of one sequence's rows, sequences, layers): b is uniform,
-  // so its position and row count come in through scalar loads; layer z
-  // has its pools layer_pool elements and its rows layer_rows elements on
+  // grid (blocks, sequences, layers): b is uniform, so its position and row
+  // count come in through scalar loads; layer z has its pools layer_pool
+  // elements and its rows layer_rows elements on.
   k_pages = static_cast<E*>(k_pages) + blockIdx.z * layer_pool;
   v_pages = static_cast<E*>(v_pages) + blockIdx.z * layer_pool;
   k += blockIdx.z * layer_rows;
   v += blockIdx.z * layer_rows;
   const int b = blockIdx.y;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * per_row) return;
-  const int c = idx % (D / KP);
-  const int g = (idx / (D / KP)) % Hkv;
-  const int r = idx / per_row;
-  // the row's K/V values do not depend on where they go: fetch them first
-  const size_t src = ((static_cast<size_t>(b) * rows + r) * Hkv + g) * D + c * KP;
-  const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src);
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src);
-  const int nr = nrows ? nrows[b] : rows;
-  if (r >= nr) return;
-  const int pos = pos0[b] + r;
-  if (pos < 0) {
-    set_dev_err(dev_err, ISD_DEV_STATE);
+  const int nr = nrows ? min(nrows[b], rows) : rows;
+  const int p0 = pos0[b];
+  if (static_cast<int>(blockIdx.x) < k_blocks) {
+    // K: one thread per (row, head, 16-byte run); a row's run is whole in
+    // the page ([D/KP][16 slots][KP]). Rows past nrows leave before loading.
+    const int per_row = Hkv * (D / KP);
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * per_row) return;
+    const int r = idx / per_row;
+    if (r >= nr) return;
+    const int c = idx % (D / KP);
+    const int g = (idx / (D / KP)) % Hkv;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(k + ((static_cast<size_t>(b) * rows + r) * Hkv + g) * D + c * KP);
+    const int pos = p0 + r;
+    if (pos < 0) {
+      set_dev_err(dev_err, ISD_DEV_STATE);
+      return;
+    }
+    const int col = pos >> 4, slot = pos & 15;
+    if (col >= table_stride) {
+      set_dev_err(dev_err, ISD_DEV_CAPACITY);
+      return;
+    }
+    const int pid = block_table[static_cast<size_t>(b) * table_stride + col];
+    if (pid < 0 || pid >= num_pages) {
+      set_dev_err(dev_err, ISD_DEV_PAGE_OOB);
+      return;
+    }
+    E* kpage = static_cast<E*>(k_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
+    *reinterpret_cast<u32x4*>(kpage + (c * 16 + slot) * KP) = kv;
     return;
   }
-  const int col = pos >> 4, slot = pos & 15;
-  if (col >= table_stride) {
-    set_dev_err(dev_err, ISD_DEV_CAPACITY);
-    return;
-  }
+  // V: the page keeps the 8 slots of a half page contiguous per dimension
+  // ([2 halves][D][8 slots]), so one thread per (half page, head, dimension)
+  // rewrites that 8-slot run whole: it reads it, replaces the slots of the
+  // rows being written and stores it back (whole runs instead of 2-byte
+  // scatters). Unit u is the (u+1)-th half page from the one holding pos0.
+  // Positions the K threads flag (negative, past the table, bad page) are
+  // skipped here; slots of other positions keep their values. Two sequences
+  // must not write into one page in the same call.
+  const int idx = (blockIdx.x - k_blocks) * blockDim.x + threadIdx.x;
+  const int d = idx % D;
+  const int g = (idx / D) % Hkv;
+  const int u = idx / (D * Hkv);
+  if (u >= v_units) return;
+  const int first = ((p0 >> 3) + u) * 8;  // first position of the half page
+  const int lo = max(max(p0, first), 0), hi = min(p0 + nr, first + 8);
+  if (lo >= hi) return;
+  const int col = first >> 4;
+  if (col >= table_stride) return;
   const int pid = block_table[static_cast<size_t>(b) * table_stride + col];
-  if (pid < 0 || pid >= num_pages) {
-    set_dev_err(dev_err, ISD_DEV_PAGE_OOB);
-    return;
-  }
-  E* kpage = static_cast<E*>(k_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
-  E* vpage = static_cast<E*>(v_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16);
-  *reinterpret_cast<u32x4*>(kpage + (c * 16 + slot) * KP) = kv;
-  const E* ve = reinterpret_cast<const E*>(&vv);
+  if (pid < 0 || pid >= num_pages) return;
+  E* run = static_cast<E*>(v_pages) + (static_cast<size_t>(pid) * Hkv + g) * (D * 16) + (((first >> 3) & 1) * D + d) * 8;
+  constexpr int kVecs = 8 * static_cast<int>(sizeof(E)) / 16;
+  u32x4 w[kVecs];
 #pragma unroll
-  for (int j = 0; j < KP; ++j) vpage[((slot >> 3) * D + c * KP + j) * 8 + (slot & 7)] = ve[j];
+  for (int i = 0; i < kVecs; ++i) w[i] = reinterpret_cast<const u32x4*>(run)[i];
+  E* ev = reinterpret_cast<E*>(w);
+  const E* vrow = v + (static_cast<size_t>(b) * rows * Hkv + g) * D + d;  // row 0 of this head and dimension
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int pos = first + j;
+    if (pos >= lo && pos < hi) ev[j] = vrow[static_cast<size_t>(pos - p0) * Hkv * D];
+  }
+#pragma unroll
+  for (int i = 0; i < kVecs; ++i) reinterpret_cast<u32x4*>(run)[i] = w[i];
 }
 
 }  // namespace isd
@@ -979,12 +1012,19 @@ int kv_write_call(const isd_kv_cache* kv, int layers, int64_t layer_stride, cons
   const int KP = kv->dtype == ISD_BF16 ? 8 : 4;
   const long per_seq = static_cast<long>(rows) * kv->num_kv_heads * (D / KP);
   const long layer_rows = static_cast<long>(C) * rows * kv->num_kv_heads * D;
-  const dim3 grid(static_cast<unsigned>((per_seq + 255) / 256), static_cast<unsigned>(C), static_cast<unsigned>(layers));
+  // K blocks first, then V blocks: `rows` consecutive positions touch at
+  // most (rows + 7) / 8 + 1 half pages
+  const int k_blocks = static_cast<int>((per_seq + 255) / 256);
+  const int v_units = (rows + 7) / 8 + 1;
+  const long v_threads = static_cast<long>(v_units) * kv->num_kv_heads * D;
+  const long blocks = k_blocks + (v_threads + 255) / 256;
+  if (blocks > INT_MAX) return ISD_E_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(C), static_cast<unsigned>(layers));
 #define ISD_KVW(E, DD)                                                                                          \
   hipLaunchKernelGGL((kv_write_kernel<E, DD>), grid, dim3(256), 0, stream, kv->k_pages, kv->v_pages,            \
                      kv->block_table, kv->table_stride, kv->num_pages, kv->num_kv_heads, static_cast<const E*>(k), \
                      static_cast<const E*>(v), pos0, nrows, C, rows, dev_err, static_cast<long>(layer_stride),    \
-                     layer_rows)
+                     layer_rows, k_blocks, v_units)
   if (kv->dtype == ISD_BF16) {
     if (D == 128) ISD_KVW(uint16_t, 128);
     else ISD_KVW(uint16_t, 64);
