@@ -108,7 +108,10 @@ typedef struct isd_kv_cache {
  * position pos0[b] + r. k and v are [C][rows][Hkv][D] in kv->dtype.
  * nrows may be NULL (every sequence writes `rows` rows). Positions whose
  * page column is >= table_stride or whose page id is outside the pool are
- * skipped and flagged (ISD_DEV_CAPACITY / ISD_DEV_PAGE_OOB). C <= 65535
+ * skipped and flagged (ISD_DEV_CAPACITY / ISD_DEV_PAGE_OOB); a negative
+ * position is skipped and flagged ISD_DEV_STATE. Every other slot of the
+ * pages keeps its value. Two sequences of one call must not write into the
+ * same page (a page's V slots are rewritten in runs of 8). C <= 65535
  * (else ISD_E_UNSUPPORTED); k and v must be 16-byte aligned. */
 int isd_kv_write(const isd_kv_cache* kv, const void* k, const void* v,
                  const int32_t* pos0, const int32_t* nrows, int C, int rows,
