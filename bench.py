@@ -422,8 +422,9 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n, "launches": 3}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); nothing in this build runs on "
-              "several GPUs", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU "
+              "path; the step shards over sequences with no exchange, so N GPUs run N copies of it",
+              file=sys.stderr)
         sys.exit(2)
 
     import draft_verify_decoding_amd as dvd
