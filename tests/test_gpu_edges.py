@@ -130,3 +130,37 @@ def test_smallest_projections(M, K, Nout, r):
     assert np.abs(got - want).max() / np.abs(want).max() < 2e-3
     m = torch.from_numpy(mask).to(DEV)
     assert torch.equal(y[~m].view(torch.int32), base[~m].view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_kv_write_keeps_every_other_slot(dtype, D):
+    """Pools filled with random values; blocks that start inside a half page,
+    cross a half page, cross a page and start on a page boundary, with 8, 3,
+    1 and 8 rows, are written: the written slots hold the rows (documented
+    layout: K [page][head][D/KP][16 slots][KP], V [page][head][2 halves][D]
+    [8 slots]) and every other element of both pools keeps its bits."""
+    Hkv, rows = 2, 8
+    pos0 = np.array([5, 13, 16, 30], dtype=np.int32)
+    nrows = np.array([8, 3, 1, 8], dtype=np.int32)
+    case = workload.AttentionCase(67, C=4, rows=rows, Hq=2, Hkv=Hkv, D=D, ctx=pos0.tolist(), dtype=dtype)
+    kv = dvd.KVCache(case.num_pages, Hkv, D, dtype, torch.from_numpy(case.table), DEV)
+    kv.k_pages.copy_(workload.normal(tuple(kv.k_pages.shape), 1.0, dtype, "cpu", 67, "kpool").to(DEV))
+    kv.v_pages.copy_(workload.normal(tuple(kv.v_pages.shape), 1.0, dtype, "cpu", 67, "vpool").to(DEV))
+    k = workload.normal((4, rows, Hkv, D), 1.0, dtype, "cpu", 67, "k")
+    v = workload.normal((4, rows, Hkv, D), 1.0, dtype, "cpu", 67, "v")
+    P, KP = case.num_pages, 16 // (2 if dtype == torch.bfloat16 else 4)
+    want_k = kv.k_pages.cpu().clone().reshape(P, Hkv, D // KP, 16, KP)
+    want_v = kv.v_pages.cpu().clone().reshape(P, Hkv, 2, D, 8)
+    for b in range(4):
+        for r in range(int(nrows[b])):
+            pos = int(pos0[b]) + r
+            page, slot = case.table[b, pos // 16], pos % 16
+            want_k[page, :, :, slot, :] = k[b, r].reshape(Hkv, D // KP, KP)
+            want_v[page, :, slot // 8, :, slot % 8] = v[b, r]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dvd.isd_kv_write(kv, k.to(DEV), v.to(DEV), torch.from_numpy(pos0).to(DEV), torch.from_numpy(nrows).to(DEV),
+                     dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(kv.k_pages.cpu().reshape(want_k.shape), want_k)
+    assert torch.equal(kv.v_pages.cpu().reshape(want_v.shape), want_v)
