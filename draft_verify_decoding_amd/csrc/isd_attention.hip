@@ -32,6 +32,11 @@
 //    results do not depend on scheduling.
 //  * The block's own K/V may come from its rows instead of the pages
 //    (isd_attention_with_block): only the boundary tiles read them.
+//  * When a KV head has more than 32 query columns (MB > 1 waves per head,
+//    bf16), its waves share each K/V tile through LDS: each direct-loads a
+//    share of the tile's 1 KB runs, so a K/V byte enters the CU once.
+//  * In the chunked split, the chunks of all sequences go to consecutive
+//    workgroups, so the XCDs (workgroup id mod 8) get equal counts.
 #include "isd_common.hpp"
 
 #include <algorithm>
