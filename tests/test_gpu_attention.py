@@ -403,3 +403,25 @@ def test_timed_launch_configuration_against_the_oracle(shape):
     kp, vp = oracle_pages(case)
     want = ref.block_attention(to64(case.q)[seqs], kp, vp, case.table[seqs], case.ctx[seqs])
     assert slab_errors(got.cpu().double().numpy()[seqs], want).max() < 2e-3
+
+
+@pytest.mark.parametrize("split", ["chunked", "stream-K"])
+def test_bad_sequences_inside_the_batch_leave_the_others_exact(split):
+    """A sequence with ctx = -1 (ISD_DEV_STATE) sits in the middle of the
+    batch and, in the chunked split, another one exceeds max_len
+    (ISD_DEV_CAPACITY): both have no work, so the chunks or tiles of every
+    later sequence move to other workgroups. The flags are raised and every
+    other sequence matches the oracle."""
+    case = workload.AttentionCase(48, C=5, rows=8, Hq=8, Hkv=2, D=64, ctx=[300, 50, 2000, 900, 64])
+    kv, err = fill_cache(case)
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    ctx[1] = -1
+    chunked = split == "chunked"
+    out = dvd.isd_attention(kv, case.q.to(DEV), ctx, max_len=1000 if chunked else int(case.lengths.max()),
+                            slices=dvd.attn_invariant(2) if chunked else 0, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == (dvd.DEV_STATE | dvd.DEV_CAPACITY if chunked else dvd.DEV_STATE)
+    good = np.array([0, 3, 4] if chunked else [0, 2, 3, 4])
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q)[good], kp, vp, case.table[good], case.ctx[good])
+    assert slab_errors(out.cpu().double().numpy()[good], want).max() < 2e-3
