@@ -364,7 +364,10 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=
               f"{accept_steps} steps from FRESH at V={V}, {t_acc / seq_steps * 1e3:.1f} ms per "
               f"sequence-step, {tok_per_seq_step:.3f} tokens per sequence-step; "
               f"{t_fwd + t_acc:.1f} s of timed CPU work")
-    return dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle", sample=sample)
+    # cores: the threads the oracle's BLAS actually ran with; beside it the
+    # host's cores as the process sees them (affinity) and as the OS counts them
+    return dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle", sample=sample,
+                host_cores_affinity=len(os.sched_getaffinity(0)), host_cores_os=os.cpu_count())
 
 
 def main():

@@ -653,8 +653,13 @@ __global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p)
   // ns reads everybody's results with device-coherent loads.
   __shared__ int s_last;
   if (threadIdx.x == 0) {
+    // the compiler may not move the slice stores past the wait, nor the
+    // counter update above it; the wait makes the stores complete first
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
     s_last = __hip_atomic_fetch_add(&p.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.ns - 1;
+    asm volatile("" ::: "memory");
   }
   __syncthreads();
   if (!s_last) return;

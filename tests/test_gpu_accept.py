@@ -39,6 +39,8 @@ class Trajectory:
         # GPU side
         self.g_in, self.g_out = dvd.SeqState(C, N), dvd.SeqState(C, N)
         self.g_ctx = self.ctx0.clone()
+        # the device commit: isd_accept adds kv_commit to this tensor itself
+        self.g_ctx_dev = self.ctx0.to(torch.int32).to(DEV)
         self.g_prev = None
         # oracle side
         self.o_n = np.zeros(C, np.int64)
@@ -63,7 +65,7 @@ class Trajectory:
             lg = padded
         lg = lg.to(DEV)
         out = dvd.isd_accept(lg, self.g_prev, self.g_in, self.g_out, N, self.seed, step, V=self.V,
-                             diag=True, dev_err=self.err, proposal=self.proposal)
+                             diag=True, dev_err=self.err, proposal=self.proposal, ctx=self.g_ctx_dev)
         torch.cuda.synchronize()
         assert self.err.item() == 0
         g = {k: getattr(out, k).cpu().numpy() for k in
@@ -90,23 +92,27 @@ class Trajectory:
             self.compared += 1
             self.flagged_agree += int(flags[b])
 
+        # the commit the device made to ctx equals the oracle's ctx + kv_commit
+        # on every sequence still compared
+        o_ctx_next = self.o_ctx.numpy() + o["kv_commit"]
+        g_ctx_next = self.g_ctx_dev.cpu().numpy()
+        act = self.active
+        assert np.array_equal(g_ctx_next[act], o_ctx_next[act]), step
         # the next step's block, assembled on the device from the device's
-        # outputs and by the oracle from its own: equal on every sequence
-        # still compared
-        g_ctx_next = (self.g_ctx + torch.from_numpy(g["kv_commit"]).long()).to(torch.int32).to(DEV)
-        tok, pos, msk = dvd.isd_block_assemble(self.g_out, out.emit, out.n_emit, g_ctx_next, N, self.V,
+        # outputs (and its committed ctx) and by the oracle from its own:
+        # equal on every sequence still compared
+        tok, pos, msk = dvd.isd_block_assemble(self.g_out, out.emit, out.n_emit, self.g_ctx_dev, N, self.V,
                                                dev_err=self.err)
         torch.cuda.synchronize()
         assert self.err.item() == 0
         o_tok, o_pos, o_msk = ref.block_assemble(o["n_draft_next"], o["drafts_next"], o["emit"], o["n_emit"],
-                                                 self.o_ctx.numpy() + o["kv_commit"], N, self.V)
-        act = self.active
+                                                 o_ctx_next, N, self.V)
         assert np.array_equal(tok.cpu().numpy()[act], o_tok[act])
         assert np.array_equal(pos.cpu().numpy()[act], o_pos[act])
         assert np.array_equal(msk.cpu().numpy()[act].astype(bool), o_msk[act])
 
         # advance both sides
-        self.g_ctx += torch.from_numpy(g["kv_commit"]).long()
+        self.g_ctx = torch.from_numpy(g_ctx_next.astype(np.int64))
         self.g_in, self.g_out = self.g_out, self.g_in
         self.g_prev = lg
         self.o_ctx += torch.from_numpy(o["kv_commit"])
@@ -448,7 +454,11 @@ def test_graph_replay_of_the_device_step_matches_eager():
     from device memory, block assembly, step advance) captured as two HIP
     graphs (even and odd steps swap the state and logits buffers) and
     replayed for 12 steps gives the same bits as the same calls run eagerly
-    with explicit step numbers. Eager work (the next logits) and host
+    with explicit step numbers, and the oracle, stepping its own state on
+    the same logits, agrees with every replay (accepted lengths, emitted
+    ids, the committed ctx, the next drafts and their q(x), the assembled
+    block), except on draws within 1e-5 of a boundary, after which that
+    sequence leaves the comparison. Eager work (the next logits) and host
     synchronisations run between the replays; every replay is checked."""
     C, N, V, seed, steps = 64, 4, 4096, 31, 12
     R, mask_id = 2 * N, V
@@ -487,6 +497,14 @@ def test_graph_replay_of_the_device_step_matches_eager():
     step_t.zero_()
 
     prev_e = None
+    # the oracle's own state, stepped on the same logits
+    o_n = np.zeros(C, np.int64)
+    o_drafts = np.full((C, N - 1), -1, np.int64)
+    o_qrow = np.zeros(C, np.int64)
+    o_ctx = ctx0.cpu().numpy().astype(np.int64)
+    o_prev = None
+    active = np.ones(C, bool)
+    compared = 0
     for t in range(steps):
         par = t % 2
         lg = teacher.block(t, e["ctx"].long(), ctx0, e["st"][par].n_draft.long(), R).contiguous()
@@ -506,5 +524,37 @@ def test_graph_replay_of_the_device_step_matches_eager():
                                b.view(torch.int32) if b.is_floating_point() else b), (t, k)
         for k in ("ctx", "tok", "pos", "msk"):
             assert torch.equal(e[k], gs[k]), (t, k)
+        # the replayed graph against the oracle
+        lo = lg.float().double().cpu().numpy()
+        o = ref.accept_step(lo, o_prev, o_n, o_drafts, o_qrow, philox.step_uniforms(seed, t, C, N), N)
+        flags = ref.flagged(o, PROB_TOL)
+        o_ctx_next = o_ctx + o["kv_commit"]
+        o_tok, o_pos, o_msk = ref.block_assemble(o["n_draft_next"], o["drafts_next"], o["emit"], o["n_emit"],
+                                                 o_ctx_next, N, mask_id)
+        g_out, g_st = gs["out"], gs["st"][1 - par]
+        g = {k: getattr(g_out, k).cpu().numpy() for k in ("accepted", "n_emit", "emit", "kv_commit")}
+        g.update({k: getattr(g_st, k).cpu().numpy() for k in ("n_draft", "drafts", "q_x", "q_row")})
+        g_ctx, g_tok = gs["ctx"].cpu().numpy(), gs["tok"].cpu().numpy()
+        g_pos, g_msk = gs["pos"].cpu().numpy(), gs["msk"].cpu().numpy().astype(bool)
+        for b in np.flatnonzero(active):
+            same = (g["accepted"][b] == o["accepted"][b] and g["n_emit"][b] == o["n_emit"][b]
+                    and g["kv_commit"][b] == o["kv_commit"][b] and np.array_equal(g["emit"][b], o["emit"][b])
+                    and g["n_draft"][b] == o["n_draft_next"][b] and g["q_row"][b] == o["q_row_next"][b]
+                    and np.array_equal(g["drafts"][b], o["drafts_next"][b]))
+            if not same:
+                assert flags[b], (t, b)
+                active[b] = False
+                continue
+            assert g_ctx[b] == o_ctx_next[b], (t, b)
+            assert np.array_equal(g_tok[b], o_tok[b]) and np.array_equal(g_pos[b], o_pos[b]), (t, b)
+            assert np.array_equal(g_msk[b], o_msk[b]), (t, b)
+            if o["n_draft_next"][b] == N - 1:
+                assert np.all(np.abs(g["q_x"][b] - o["q_x_next"][b]) <= PROB_TOL), (t, b)
+            compared += 1
+        o_n, o_drafts, o_qrow, o_ctx, o_prev = (o["n_draft_next"], o["drafts_next"], o["q_row_next"], o_ctx_next,
+                                                lo)
+    print(f"graph replay: {compared} sequence-steps equal to the oracle, {C - active.sum()} left on flagged draws",
+          flush=True)
+    assert active.sum() >= C - 4
     # the trajectory moved: FULL steps happened and tokens were emitted
     assert int(e["ctx"].sum() - ctx0.sum()) > C * steps

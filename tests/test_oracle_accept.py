@@ -214,7 +214,7 @@ def test_closed_form_matches_printed_values():
         assert chain.tpf_closed_form(N, 0.0) == pytest.approx(1.0)
 
 
-@pytest.mark.parametrize("N,p", [(4, 0.9), (4, 0.5), (2, 0.9), (8, 0.7), (3, 0.5)])
+@pytest.mark.parametrize("N,p", [(4, 0.9), (4, 0.5), (2, 0.9), (8, 0.7), (3, 0.5), (6, 0.9), (6, 0.5)])
 def test_bernoulli_chain_reproduces_closed_form(N, p):
     rng = np.random.default_rng(N * 100 + int(p * 10))
     steps = 200000
@@ -223,7 +223,7 @@ def test_bernoulli_chain_reproduces_closed_form(N, p):
     assert abs(tpf - chain.tpf_closed_form(N, p)) < 5 * N / np.sqrt(steps) + 0.01
 
 
-@pytest.mark.parametrize("N,p", [(4, 0.9), (3, 0.7)])
+@pytest.mark.parametrize("N,p", [(4, 0.9), (3, 0.7), (2, 0.5), (6, 0.9), (8, 0.7)])
 def test_oracle_accept_loop_reproduces_closed_form(N, p):
     """Run the oracle's own accept step as a decoding loop over C sequences:
     clean rows are a fixed P, MASK rows a fixed Q with sum min(P, Q) = p, so
