@@ -216,7 +216,7 @@ def dry_run(cfg, steps_total, ctx0, dev):
     ctx0_t = torch.from_numpy(ctx0.astype(np.int64)).to(dev)
     ctx = torch.from_numpy(ctx0.astype(np.int32)).to(dev)
     s_in, s_out = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
-    ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
+    ws = dvd.accept_workspace(C, N, V, R, device=dev)
     logits, ctxs, nds, accs = [], [], [], []
     prev = None
     for t in range(steps_total):
@@ -269,7 +269,7 @@ def lm_head_leg(cfg, dev, calls=20):
 
     us = timed(call, calls)
     s_in, s_out = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
-    acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, 2 * N), dtype=torch.uint8, device=dev)
+    acc_ws = dvd.accept_workspace(C, N, V, 2 * N, device=dev)
     acc_out = dvd.AcceptOutputs(C, N, 2 * N, dev, diag=False)
     lg3, st3 = logits.view(C, 2 * N, V), stats.view(C, 2 * N, nch, 2)
     own = timed(lambda: dvd.isd_accept(lg3, None, s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws), calls)
@@ -473,7 +473,7 @@ def main():
                                       v_blk=lay["v"] if commit_mode else None),
             o=lg("o", lay["xo"])))
     s_a, s_b = dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)
-    acc_ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=dev)
+    acc_ws = dvd.accept_workspace(C, N, V, R, device=dev)
     acc_out = dvd.AcceptOutputs(C, N, R, dev, diag=False)
     # commit mode: the contexts before the accept advances them are the
     # positions of the rows to commit, kv_commit their count

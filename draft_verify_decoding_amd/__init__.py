@@ -283,6 +283,11 @@ def isd_accept_workspace_size(C, N, V, rows):
     return int(lib().isd_accept_workspace_size(C, N, V, rows))
 
 
+def accept_workspace(C, N, V, rows, device="cuda"):
+    """An isd_accept workspace (its contents on entry are ignored)."""
+    return torch.empty(isd_accept_workspace_size(C, N, V, rows), dtype=torch.uint8, device=device)
+
+
 class AcceptOutputs:
     def __init__(self, C, N, rows, device, diag):
         self.accepted = torch.empty(C, dtype=torch.int32, device=device)
@@ -311,9 +316,8 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     V = ld if V is None else V
     if out is None:
         out = AcceptOutputs(C, N, rows, logits.device, diag)
-    need = isd_accept_workspace_size(C, N, V, rows)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        ws = accept_workspace(C, N, V, rows, logits.device)
     args = IsdAcceptArgs()
     args.C, args.N, args.V, args.rows = C, N, V, rows
     args.dtype = _dtype_code(logits)

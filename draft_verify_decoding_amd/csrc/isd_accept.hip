@@ -10,32 +10,38 @@
 // the FULL/FRESH alternation are what reproduce the page's tokens-per-forward
 // closed form ("Speedup Factor Explorer").
 //
-// Two launches, both HBM-streaming and deterministic:
-//   stats   one pass over every logits row the step may read: per 8192-entry
-//           chunk, the max and sum of exp(l - max) (fp32 from exact bf16);
-//           a workgroup takes two chunks with all their loads in flight.
-//   sample  grid (slices, sequences). Every workgroup rebuilds the row
-//           statistics and the accept decision from the chunk stats (same
-//           fixed-order arithmetic, so all agree). On a rejection each slice
-//           sums the residual max(0, P_a - Q_{a+1}) over its chunk; when all
-//           drafts pass, slice k rescans the one chunk where the CDF of row
-//           n + k crosses its uniform (bonus for k = 0, proposals after).
-//           The last workgroup of a sequence to finish (a counter per
-//           sequence, zeroed by the stats launch) then picks and rescans the
-//           residual chunk and writes the outputs and the next state.
+// Two launches:
+//   stats   one workgroup per 8192-entry chunk of every logits row the step
+//           reads: the chunk's max and sum of exp(l - max) (fp32 from exact
+//           bf16), streamed with non-temporal loads; the workgroup whose
+//           chunk holds a pending draft also records that draft's logit in
+//           its verify row. Nothing else: the launch is a pure stream.
+//   decide  grid (slices, sequences). Every workgroup of a sequence merges
+//           the chunk statistics into row statistics and takes the accept
+//           decision (same fixed-order arithmetic, so all agree); slice 0
+//           writes the outputs the decision alone fixes. Then:
+//           - all drafts pass: slice k draws row n + k (the bonus for k = 0,
+//             proposal k after) from one rescanned chunk and writes it;
+//           - a draft is rejected: slice k sums max(0, P_a - Q_{a+1}) over
+//             one chunk; the last slice of the sequence to count itself in
+//             (a counter per sequence, cleared by the stats launch) picks
+//             the chunk of the residual draw, rescans it and writes the
+//             token. Slice sums go through agent-scope atomic stores and
+//             loads; a writer waits for its stores to complete before it
+//             counts itself in.
 // When the caller passes the chunk statistics (isd_lm_head wrote them with
-// the logits), a small launch that zeroes the counters replaces the stats
-// launch.
+// the logits), a small launch that clears the counters and gathers the
+// drafts' logits replaces the stats launch.
 #include "isd_common.hpp"
 
 namespace isd {
 
 constexpr int kChunk = kVocabChunk;  // vocab entries per stats chunk
-constexpr int kThreads = 256;    // threads per workgroup
-constexpr int kPerThread = 32;   // entries per thread in a chunk
-constexpr int kStatsChunks = 2;  // chunks per workgroup of the stats launch
+constexpr int kThreads = 256;        // threads per workgroup
+constexpr int kPerThread = 32;       // entries per thread in a chunk
+constexpr int kResidChunks = 1;      // chunks per residual slice
 constexpr int kMaxN = 8;
-constexpr int kMaxChunks = 64;   // vocabularies up to 524,288 entries
+constexpr int kMaxChunks = 64;  // vocabularies up to 524,288 entries
 static_assert(kThreads * kPerThread == kChunk, "chunk tiling");
 
 struct AcceptParams {
@@ -48,35 +54,27 @@ struct AcceptParams {
   const uint64_t* step_dev;  // when set, the step number comes from here
   int32_t *accepted, *n_emit, *emit, *kv_commit, *ctx;
   float *p_x, *resid_mass, *row_m, *row_s;
-  float2* stats;    // [C][rows][nch] (chunk max, chunk sum)
-  float* resid;     // [C][nch] residual sum per chunk
-  int2* samp;       // [C][N] (token, bits of q(x)) from the sample kernel
-  int* arrive;      // [C] workgroups of the sample launch done, per sequence
+  float2* stats;  // [C][rows][nch] (chunk max, chunk sum), or the given ones
+  float* lx;      // [C][kMaxN] logit of draft j+1 in verify row j
+  float* resid;   // [C][nch] residual sum per chunk
+  int* arrive;    // [C] workgroups of the decide launch done, per sequence
   int32_t* dev_err;
-  int argmax;       // proposals are argmax q (a point mass at the draft)
-  int stats_given;  // stats come from the caller (isd_lm_head): no statistics pass
+  int argmax;  // proposals are argmax q (a point mass at the draft)
 };
 
-// ------------------------------------------- values handed between workgroups
-// The slice results of the sample launch reach the sequence's last
-// workgroup through device-coherent (agent-scope) atomic stores and loads,
-// so no cache-wide writeback or invalidate is needed: the writer waits for
-// its store to complete before it counts itself in.
+// --------------------------------------- values handed between workgroups
+// Device-coherent (agent-scope) stores and loads; the writer makes its
+// stores complete (stores_done) before it counts itself in.
+__device__ __forceinline__ void stores_done() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void put_f32(float* ptr, float v) {
   __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float get_f32(float* ptr) {
   return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_sample(int2* ptr, int tok, float q) {
-  const unsigned long long v =
-      static_cast<unsigned long long>(static_cast<uint32_t>(tok)) | (static_cast<unsigned long long>(__float_as_uint(q)) << 32);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(ptr), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int2 get_sample(int2* ptr) {
-  const unsigned long long v =
-      __hip_atomic_load(reinterpret_cast<unsigned long long*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_int2(static_cast<int>(static_cast<uint32_t>(v)), static_cast<int>(static_cast<uint32_t>(v >> 32)));
 }
 
 // ------------------------------------------------------------ Philox4x64-10
@@ -105,6 +103,10 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint6
 __device__ __forceinline__ float uniform_of(uint64_t w0) {
   return (static_cast<float>(static_cast<uint32_t>(w0 >> 41)) + 0.5f) * 0x1p-23f;
 }
+__device__ __forceinline__ float slot_uniform(const AcceptParams& p, int slot, int b) {
+  const uint64_t step = p.step_dev ? *p.step_dev : p.step;
+  return uniform_of(philox_word0(static_cast<uint64_t>(slot), static_cast<uint64_t>(b), step, 0ull, p.seed, 0ull));
+}
 
 // -------------------------------------------------------------- arithmetic
 // weight_of, prob_of and merge_ms (isd_common.hpp) are the only places that
@@ -120,25 +122,90 @@ __device__ __forceinline__ float load_elem(const E* row, int v) {
   return Elem<E>::to_f32(row[v]);
 }
 
-// Load this thread's 32 entries of chunk c (entries >= V become -inf).
+// This thread's 32 entries of a chunk, kept packed as loaded (bf16 pairs
+// or fp32 words); at(k) unpacks entry k exactly. Keeping the rows packed
+// and recomputing weights where they are needed holds the register
+// footprint of the rescans down.
 template <typename E>
-__device__ __forceinline__ void load_chunk_slice(const E* row, int V, int c, float (&x)[kPerThread]) {
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  static constexpr uint32_t kNegInf = 0xff80ff80u;  // two bf16 -inf
+  u32x4 v[kPerThread / 8];
+  __device__ __forceinline__ float at(int k) const {
+    const uint32_t w = v[k >> 3][(k >> 1) & 3];
+    return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  // opaque to the optimiser: values recomputed after this are not reused
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int q = 0; q < kPerThread / 8; ++q) asm volatile("" : "+v"(v[q]));
+  }
+};
+template <>
+struct Raw<float> {
+  u32x4 v[kPerThread / 4];
+  __device__ __forceinline__ float at(int k) const { return __uint_as_float(v[k >> 2][k & 3]); }
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q) asm volatile("" : "+v"(v[q]));
+  }
+};
+
+// 16 bytes of entries v0 .. v0 + KP - 1 of a row; entries >= V read as -inf.
+// NT: a streaming (non-temporal) load, for data read once.
+template <bool NT = false>
+__device__ __forceinline__ u32x4 load_vec(const uint16_t* row, int V, int v0) {
+  if (v0 + 8 <= V) {
+    const u32x4* ptr = reinterpret_cast<const u32x4*>(row + v0);
+    return NT ? __builtin_nontemporal_load(ptr) : *ptr;
+  }
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v0 + 2 * i < V ? row[v0 + 2 * i] : 0xff80u;
+    const uint32_t hi = v0 + 2 * i + 1 < V ? row[v0 + 2 * i + 1] : 0xff80u;
+    w[i] = lo | (hi << 16);
+  }
+  return w;
+}
+template <bool NT = false>
+__device__ __forceinline__ u32x4 load_vec(const float* row, int V, int v0) {
+  if (v0 + 4 <= V) {
+    const u32x4* ptr = reinterpret_cast<const u32x4*>(row + v0);
+    return NT ? __builtin_nontemporal_load(ptr) : *ptr;
+  }
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = v0 + i < V ? __float_as_uint(row[v0 + i]) : __float_as_uint(-INFINITY);
+  return w;
+}
+
+// Entries c*kChunk + 32t .. +31 of chunk c go to thread t (token order
+// within a thread, as the inverse-CDF search needs).
+template <typename E>
+__device__ __forceinline__ Raw<E> load_slice(const E* row, int V, int c) {
   constexpr int KP = Elem<E>::kPerVec;
+  Raw<E> r;
   const int v0 = c * kChunk + threadIdx.x * kPerThread;
 #pragma unroll
-  for (int q = 0; q < kPerThread / KP; ++q) {
-    const int vq = v0 + q * KP;
-    if (vq + KP <= V) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(row + vq);
-      float f[KP];
-      unpack16(w, f);
+  for (int q = 0; q < kPerThread / KP; ++q) r.v[q] = load_vec(row, V, v0 + q * KP);
+  return r;
+}
+
+// Entries c*kChunk + i*kThreads*KP + KP*t .. +KP-1 of chunk c go to thread
+// t: each load instruction of the workgroup reads 4 KB of contiguous logits.
+// (A chunk's max and sum do not depend on which thread holds what.) The
+// statistics pass reads every row once: streaming loads, which measured
+// twice as fast as cached ones on a cold 130 MB batch of rows.
+template <typename E>
+__device__ __forceinline__ Raw<E> load_coalesced(const E* row, int V, int c) {
+  constexpr int KP = Elem<E>::kPerVec;
+  Raw<E> r;
 #pragma unroll
-      for (int k = 0; k < KP; ++k) x[q * KP + k] = f[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < KP; ++k) x[q * KP + k] = (vq + k < V) ? load_elem(row, vq + k) : -INFINITY;
-    }
-  }
+  for (int q = 0; q < kPerThread / KP; ++q)
+    r.v[q] = load_vec<true>(row, V, c * kChunk + q * kThreads * KP + threadIdx.x * KP);
+  return r;
 }
 
 // Workgroup reduction of (max, sum) pairs in a fixed tree.
@@ -192,158 +259,18 @@ __device__ __forceinline__ float block_exclusive_scan(float v) {
   return base + excl;
 }
 
-// ============================================================ stats kernel
-// Entries c*kChunk + i*2048 + 8t .. +7 (i = 0..3) of chunk c go to thread t:
-// each load instruction of the workgroup reads 4 KB of contiguous logits.
-// (A chunk's max and sum do not depend on which thread holds what; the
-// sampling rescans keep token order per thread.)
-template <typename E>
-__device__ __forceinline__ void load_chunk_coalesced(const E* row, int V, int c, float (&x)[kPerThread]) {
-  constexpr int KP = Elem<E>::kPerVec;  // 8 bf16 or 4 fp32 per 16 bytes
-#pragma unroll
-  for (int q = 0; q < kPerThread / KP; ++q) {
-    const int vq = c * kChunk + q * kThreads * KP + threadIdx.x * KP;
-    if (vq + KP <= V) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(row + vq);
-      float f[KP];
-      unpack16(w, f);
-#pragma unroll
-      for (int k = 0; k < KP; ++k) x[q * KP + k] = f[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < KP; ++k) x[q * KP + k] = (vq + k < V) ? load_elem(row, vq + k) : -INFINITY;
-    }
+// (max, sum) of a row from its chunk statistics, merged in chunk order.
+__device__ __forceinline__ float2 row_ms(const float2* st, int nch) {
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c].x);
+  float S = 0.f;
+  if (M != -INFINITY) {
+    for (int c = 0; c < nch; ++c) S += st[c].y * fast_exp2((st[c].x - M) * kLog2e);
   }
+  return make_float2(M, S);
 }
-
-template <typename E>
-__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
-  const int c0 = blockIdx.x * kStatsChunks, r = blockIdx.y, b = blockIdx.z;
-  if (c0 == 0 && r == 0 && threadIdx.x == 0) p.arrive[b] = 0;  // the sample launch counts from zero
-  int n = p.in.n_draft[b];
-  n = n < 0 ? 0 : (n > p.N - 1 ? p.N - 1 : n);
-  if (r > n + p.N - 1) return;
-  const E* row = row_ptr<E>(p.logits, p.ld, p.rows, b, r);
-  float x[kStatsChunks][kPerThread];
-#pragma unroll
-  for (int h = 0; h < kStatsChunks; ++h) {
-    if (c0 + h < p.nch) {
-      load_chunk_coalesced<E>(row, p.V, c0 + h, x[h]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kPerThread; ++k) x[h][k] = -INFINITY;
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < kStatsChunks; ++h) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[h][k]);
-    float s = 0.f;
-    if (m != -INFINITY) {
-      const float ml = m * kLog2e;
-#pragma unroll
-      for (int k = 0; k < kPerThread; ++k) s += weight_of(x[h][k], ml);
-    }
-    block_reduce_ms(m, s);
-    if (threadIdx.x == 0 && c0 + h < p.nch) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c0 + h] = make_float2(m, s);
-  }
-}
-
-// With the chunk statistics given, only the arrival counters of the sample
-// launch need clearing.
-__global__ __launch_bounds__(256) void accept_arrive_reset_kernel(int* arrive, int C) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < C) arrive[b] = 0;
-}
-
-// ------------------------------------------------ shared per-sequence logic
-struct Decision {
-  int n, a, err;                     // err: ISD_DEV_* bits, 0 if the step can be taken
-  int qrow;                          // first row of the previous step that proposed
-  float M[2 * kMaxN];                // row max
-  float S[2 * kMaxN];                // row sum exp(l - M)
-  float u[2 * kMaxN];                // uniforms by slot
-  float px[kMaxN];                   // P_{j-1}(x_j) of tested drafts
-  int draft[kMaxN];                  // pending draft ids
-  float2 st[2 * kMaxN][kMaxChunks];  // chunk (max, sum) of the rows read
-};
-
-// Rebuild row statistics, uniforms and the accept decision of sequence b.
-// Every workgroup that calls this computes the same values. The state, the
-// chunk statistics of every row and the uniforms are fetched together; the
-// logits of the drafts follow in one more round trip. Result in LDS.
-template <typename E>
-__device__ void decide(const AcceptParams& p, int b, Decision& d) {
-  const int tid = threadIdx.x;
-  const int N = p.N, nd = N - 1, R = 2 * N - 1;
-  __shared__ int s_n, s_draft[kMaxN];
-  __shared__ float s_qx[kMaxN], s_pall[kMaxN];
-  if (tid == 0) {
-    s_n = p.in.n_draft[b];
-    d.qrow = p.in.q_row[b];
-  }
-  if (tid < nd) {
-    s_draft[tid] = p.in.drafts[b * nd + tid];
-    s_qx[tid] = p.in.q_x[b * nd + tid];
-    d.draft[tid] = s_draft[tid];
-  }
-  for (int i = tid; i < R * p.nch; i += kThreads)
-    d.st[i / p.nch][i % p.nch] = p.stats[(static_cast<long>(b) * p.rows + i / p.nch) * p.nch + i % p.nch];
-  if (tid < 2 * N) {
-    const uint64_t step = p.step_dev ? *p.step_dev : p.step;
-    d.u[tid] = uniform_of(philox_word0(static_cast<uint64_t>(tid), static_cast<uint64_t>(b), step, 0ull, p.seed, 0ull));
-  }
-  __syncthreads();
-  // every thread clamps n the same way; thread 0 records what was wrong
-  const int n_raw = s_n;
-  const int n = (n_raw < 0 || n_raw > nd) ? 0 : n_raw;
-  if (tid == 0) {
-    int err = 0;
-    if (n_raw < 0 || n_raw > nd) err |= ISD_DEV_STATE;
-    if (n > 0 && ((!p.argmax && !p.prev_logits) || d.qrow < 0 || d.qrow + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
-    for (int j = 0; j < n; ++j)
-      if (s_draft[j] < 0 || s_draft[j] >= p.V) err |= ISD_DEV_TOKEN_OOB;
-    d.n = n;
-    d.err = err;
-  }
-  // the logit of draft j+1 in verify row j (loaded before the row sums exist)
-  float lx = 0.f;
-  const bool draft_ok = tid < n && s_draft[tid] >= 0 && s_draft[tid] < p.V;
-  if (draft_ok) lx = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, tid), s_draft[tid]);
-  const int nrows = n + N;  // rows 0 .. n + N - 1
-  __syncthreads();
-  if (tid < nrows) {
-    float M = -INFINITY;
-    for (int c = 0; c < p.nch; ++c) M = fmaxf(M, d.st[tid][c].x);
-    float S = 0.f;
-    if (M != -INFINITY) {
-      for (int c = 0; c < p.nch; ++c) S += d.st[tid][c].y * fast_exp2((d.st[tid][c].x - M) * kLog2e);
-    }
-    d.M[tid] = M;
-    d.S[tid] = S;
-    if (!(M > -INFINITY && M < INFINITY && S > 0.f && S < INFINITY)) atomicOr(&d.err, static_cast<int>(ISD_DEV_NONFINITE));
-  }
-  __syncthreads();
-  if (tid < n) s_pall[tid] = draft_ok ? prob_of(lx, d.M[tid], d.S[tid]) : NAN;
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    for (int j = 0; j < kMaxN; ++j) d.px[j] = NAN;
-    if (!d.err) {
-      for (int j = 1; j <= n; ++j) {
-        const float px = s_pall[j - 1];
-        d.px[j - 1] = px;
-        // u * q < p compared exactly (fp32 operands, exact fp64 product).
-        if (static_cast<double>(d.u[j]) * static_cast<double>(s_qx[j - 1]) < static_cast<double>(px))
-          ++a;
-        else
-          break;
-      }
-    }
-    d.a = a;
-  }
-  __syncthreads();
+__device__ __forceinline__ bool ms_finite(float2 ms) {
+  return ms.x > -INFINITY && ms.x < INFINITY && ms.y > 0.f && ms.y < INFINITY;
 }
 
 // Residual weight max(0, P_a(v) - Q(v)) of one entry.
@@ -356,47 +283,75 @@ __device__ __forceinline__ float resid_weight(float l, float lq, float ma_l2, fl
   return fmaxf(0.f, pa - qa);
 }
 
-// Inverse-CDF search inside one chunk: weights w[] of this thread's 32
-// entries (thread order = token order), target t_rel measured from the start
-// of the chunk. Returns the smallest crossing token id, or the last token
-// with non-zero weight in the chunk when rounding leaves no crossing.
-__device__ int chunk_search(const float (&w)[kPerThread], int c, float t_rel) {
+// Inverse-CDF search inside one chunk: wf(k) is this thread's weight of
+// entry c*kChunk + 32t + k (thread order = token order), the target t_rel
+// is measured from the start of the chunk. Returns the smallest crossing
+// token id, or the last token with non-zero weight in the chunk when
+// rounding leaves no crossing; *w_tok is that token's weight. The thread
+// that holds the crossing recomputes its weights in the same order (after
+// fence()) rather than keeping all 32 of them live across the scan.
+template <typename WF>
+__device__ __forceinline__ int chunk_search(WF& wf, int c, float t_rel, float* w_tok) {
   __shared__ int s_tok, s_last;
+  __shared__ float s_wtok, s_wlast;
   if (threadIdx.x == 0) {
     s_tok = 0x7fffffff;
     s_last = -1;
   }
-  float local = 0.f;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) local += w[k];
-  const float base = block_exclusive_scan(local);  // also syncs
   const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  float local = 0.f, w_last = 0.f;
+  int last = -1;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const float w = wf(k);
+    local += w;
+    if (w > 0.f) {
+      last = v0 + k;
+      w_last = w;
+    }
+  }
+  const float base = block_exclusive_scan(local);  // also syncs
   const float tr = t_rel - base;
+  wf.fence();
+  int hit = -1;
+  float w_hit = 0.f;
   if (tr >= 0.f && local > tr) {
     float acc = 0.f;
-    int hit = -1;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-      acc += w[k];
-      if (hit < 0 && acc > tr) hit = v0 + k;
+      const float w = wf(k);
+      acc += w;
+      if (hit < 0 && acc > tr) {
+        hit = v0 + k;
+        w_hit = w;
+      }
     }
     if (hit >= 0) atomicMin(&s_tok, hit);
   }
-  int last = -1;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k)
-    if (w[k] > 0.f) last = v0 + k;
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
-  const int tok = s_tok != 0x7fffffff ? s_tok : s_last;
+  if (hit >= 0 && hit == s_tok) s_wtok = w_hit;
+  if (last >= 0 && last == s_last) s_wlast = w_last;
+  __syncthreads();
+  const bool crossed = s_tok != 0x7fffffff;
+  const int tok = crossed ? s_tok : s_last;
+  *w_tok = crossed ? s_wtok : s_wlast;
   __syncthreads();
   return tok;
 }
 
-// Choose the chunk of a row whose (rescaled) chunk sums cross u * S.
+// Softmax weight of a row's entries relative to its max (log2 units).
+template <typename E>
+struct SoftmaxWeights {
+  Raw<E> x;
+  float ml;
+  __device__ __forceinline__ float operator()(int k) const { return weight_of(x.at(k), ml); }
+  __device__ __forceinline__ void fence() { x.fence(); }
+};
+
+// Choose the chunk of a row whose (rescaled) chunk sums cross t.
 // Returns the chunk and writes the target relative to its start.
-__device__ __forceinline__ int pick_chunk_from_stats(const float2 (&st)[kMaxChunks], int nch, float M, float t,
-                                                     float* t_rel) {
+__device__ __forceinline__ int pick_chunk_from_stats(const float2* st, int nch, float M, float t, float* t_rel) {
   float run = 0.f;
   int last_nz = 0;
   for (int c = 0; c < nch; ++c) {
@@ -412,37 +367,43 @@ __device__ __forceinline__ int pick_chunk_from_stats(const float2 (&st)[kMaxChun
   return last_nz;
 }
 
-// Sample from softmax(row r) with uniform u: returns the token.
+// Sample from softmax(row r) (max M, sum S, chunk statistics st in LDS)
+// with uniform u: returns the token (every thread) and its probability.
 template <typename E>
-__device__ int sample_row(const AcceptParams& p, const Decision& d, int b, int r, float u) {
-  const float M = d.M[r], S = d.S[r];
-  float t_rel;
-  const int c = pick_chunk_from_stats(d.st[r], p.nch, M, u * S, &t_rel);
-  float x[kPerThread];
-  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
-  const float ml = M * kLog2e;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) x[k] = weight_of(x[k], ml);
-  return chunk_search(x, c, t_rel);
+__device__ __forceinline__ int sample_row(const AcceptParams& p, int b, int r, const float2* st, float M, float S,
+                                          float u, float* prob) {
+  __shared__ int s_c;
+  __shared__ float s_trel;
+  if (threadIdx.x == 0) {
+    float t_rel;
+    s_c = pick_chunk_from_stats(st, p.nch, M, u * S, &t_rel);
+    s_trel = t_rel;
+  }
+  __syncthreads();
+  const int c = s_c;
+  const float t_rel = s_trel;
+  SoftmaxWeights<E> wf{load_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c), M * kLog2e};
+  float w;
+  const int tok = chunk_search(wf, c, t_rel, &w);
+  *prob = w / S;  // = prob_of(l(tok), M, S): the same weight, divided by S
+  return tok;
 }
 
 // argmax of row r, ties to the smallest id: the first chunk whose maximum is
 // the row maximum holds it; its entries are compared exactly with that value.
 template <typename E>
-__device__ int argmax_row(const AcceptParams& p, const Decision& d, int b, int r) {
+__device__ __forceinline__ int argmax_row(const AcceptParams& p, int b, int r, const float2* st, float M) {
   __shared__ int s_tok;
-  const float M = d.M[r];
   int c = 0;
-  while (c + 1 < p.nch && d.st[r][c].x != M) ++c;
+  while (c + 1 < p.nch && st[c].x != M) ++c;
   if (threadIdx.x == 0) s_tok = 0x7fffffff;
   __syncthreads();
-  float x[kPerThread];
-  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c, x);
+  const Raw<E> x = load_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c);
   const int v0 = c * kChunk + threadIdx.x * kPerThread;
   int hit = 0x7fffffff;
 #pragma unroll
   for (int k = kPerThread - 1; k >= 0; --k)
-    if (x[k] == M) hit = v0 + k;
+    if (x.at(k) == M) hit = v0 + k;
   if (hit != 0x7fffffff) atomicMin(&s_tok, hit);
   __syncthreads();
   const int tok = s_tok;
@@ -450,220 +411,355 @@ __device__ int argmax_row(const AcceptParams& p, const Decision& d, int b, int r
   return tok;
 }
 
-// Residual weights of this thread's slice of chunk c. With argmax proposals
-// Q_{a+1} is a point mass at the rejected draft: the residual is P_a with
-// that token removed, and the previous block is not read.
+// What the residual of a sequence that rejected draft a+1 needs.
+struct ResidArgs {
+  float Ma, Sa;  // row a's statistics
+  float qm, qs;  // statistics of the q row that proposed draft a+1
+  int a, qrow, x_rej;
+};
+
+// Residual weights max(0, P_a - Q_{a+1}) of this thread's slice of chunk
+// c. With argmax proposals Q_{a+1} is a point mass at the rejected draft:
+// the residual is P_a with that token removed, and the previous block is
+// not read.
 template <typename E>
-__device__ __forceinline__ void resid_slice(const AcceptParams& p, int b, const Decision& d, int c,
-                                            float (&w)[kPerThread]) {
-  const int a = d.a;
-  float x[kPerThread], y[kPerThread];
-  load_chunk_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, a), p.V, c, x);
-  if (p.argmax) {
-    const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
-    const int x_rej = d.draft[a], v0 = c * kChunk + threadIdx.x * kPerThread;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+struct ResidWeights {
+  Raw<E> x, y;
+  float ma_l2, inv_sa, mq_l2, inv_sq;
+  int v0, x_rej, argmax;
+  __device__ __forceinline__ float operator()(int k) const {
+    const float l = x.at(k);
+    if (argmax) {
 #pragma clang fp contract(off)
-      const float pa = weight_of(x[k], ma_l2) * inv_sa;
-      w[k] = (x[k] == -INFINITY || v0 + k == x_rej) ? 0.f : pa;
+      const float pa = weight_of(l, ma_l2) * inv_sa;
+      return (l == -INFINITY || v0 + k == x_rej) ? 0.f : pa;
     }
-    return;
+    return l == -INFINITY ? 0.f : resid_weight(l, y.at(k), ma_l2, inv_sa, mq_l2, inv_sq);
   }
-  const int qrow = d.qrow + a;
-  load_chunk_slice<E>(row_ptr<E>(p.prev_logits, p.ld, p.rows, b, qrow), p.V, c, y);
-  const float ma_l2 = d.M[a] * kLog2e, inv_sa = 1.f / d.S[a];
-  const float mq_l2 = p.in.q_m[b * (p.N - 1) + a] * kLog2e, inv_sq = 1.f / p.in.q_s[b * (p.N - 1) + a];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) w[k] = (x[k] == -INFINITY) ? 0.f : resid_weight(x[k], y[k], ma_l2, inv_sa, mq_l2, inv_sq);
+  __device__ __forceinline__ void fence() {
+    x.fence();
+    y.fence();
+  }
+};
+
+template <typename E>
+__device__ __forceinline__ ResidWeights<E> resid_weights(const AcceptParams& p, int b, const ResidArgs& ra, int c) {
+  ResidWeights<E> r;
+  r.x = load_slice<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, ra.a), p.V, c);
+  if (!p.argmax) r.y = load_slice<E>(row_ptr<E>(p.prev_logits, p.ld, p.rows, b, ra.qrow + ra.a), p.V, c);
+  r.ma_l2 = ra.Ma * kLog2e;
+  r.inv_sa = 1.f / ra.Sa;
+  r.mq_l2 = ra.qm * kLog2e;
+  r.inv_sq = 1.f / ra.qs;
+  r.v0 = c * kChunk + threadIdx.x * kPerThread;
+  r.x_rej = ra.x_rej;
+  r.argmax = p.argmax;
+  return r;
 }
 
-// ====================================================== finish (one WG)
-// Outputs and next state of sequence b, run by the last workgroup of the
-// sample launch to finish for it: the residual chunk is picked from the
-// slice sums and rescanned here.
+// Pending drafts of sequence b (an invalid count reads as 0; the decide
+// launch flags it).
+__device__ __forceinline__ int seq_n(const AcceptParams& p, int b) {
+  const int n = p.in.n_draft[b];
+  return (n < 0 || n > p.N - 1) ? 0 : n;
+}
+
+// ============================================================ stats kernel
+// Grid (chunks, 2N-1 rows, sequences): chunk c of row r of sequence b, if
+// the step reads that row (rows 0 .. n+N-1).
 template <typename E>
-__device__ void finish(const AcceptParams& p, int b, const Decision& d) {
-  const int N = p.N, nd = N - 1;
-  const int tid = threadIdx.x;
-  if (d.err) {
-    if (tid == 0) {
-      p.accepted[b] = -1;
-      p.n_emit[b] = 0;
-      p.kv_commit[b] = 0;
-      for (int k = 0; k < N; ++k) p.emit[b * N + k] = -1;
-      p.out.n_draft[b] = p.in.n_draft[b];
-      p.out.q_row[b] = p.in.q_row[b];
-      for (int k = 0; k < nd; ++k) {
-        p.out.drafts[b * nd + k] = p.in.drafts[b * nd + k];
-        p.out.q_x[b * nd + k] = p.in.q_x[b * nd + k];
-        p.out.q_m[b * nd + k] = p.in.q_m[b * nd + k];
-        p.out.q_s[b * nd + k] = p.in.q_s[b * nd + k];
-      }
-      if (p.resid_mass) p.resid_mass[b] = -1.f;
-      if (p.p_x)
-        for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = NAN;
-      if (p.row_m)
-        for (int r = 0; r < p.rows; ++r) {
-          p.row_m[b * p.rows + r] = NAN;
-          p.row_s[b * p.rows + r] = NAN;
-        }
-      set_dev_err(p.dev_err, static_cast<uint32_t>(d.err));
+__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  if (c == 0 && r == 0 && threadIdx.x == 0) p.arrive[b] = 0;  // the decide launch counts from zero
+  const int n = seq_n(p, b);
+  if (r > n + p.N - 1) return;
+  const Raw<E> x = load_coalesced<E>(row_ptr<E>(p.logits, p.ld, p.rows, b, r), p.V, c);
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x.at(k));
+  float s = 0.f;
+  if (m != -INFINITY) {
+    const float ml = m * kLog2e;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) s += weight_of(x.at(k), ml);
+  }
+  // the logit of draft r+1 in verify row r, by the thread that holds it
+  if (r < n) {
+    constexpr int KP = Elem<E>::kPerVec;
+    const int o = p.in.drafts[b * (p.N - 1) + r] - c * kChunk;
+    if (o >= 0 && o < kChunk && o + c * kChunk < p.V && (o % (kThreads * KP)) / KP == static_cast<int>(threadIdx.x)) {
+      const int kk = (o / (kThreads * KP)) * KP + o % KP;
+      float l = 0.f;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k)
+        if (k == kk) l = x.at(k);
+      p.lx[b * kMaxN + r] = l;
     }
-    return;
   }
-  const int n = d.n, a = d.a;
-  __shared__ int s_t;
-  __shared__ float s_mass;
-  // the other workgroups' results, fetched in parallel
-  __shared__ float s_res[kMaxChunks];
-  __shared__ int2 s_smp[kMaxN];
-  if (a < n) {
-    if (tid < p.nch) s_res[tid] = get_f32(&p.resid[static_cast<long>(b) * p.nch + tid]);
-  } else if (tid < N) {
-    s_smp[tid] = get_sample(&p.samp[b * N + tid]);
+  block_reduce_ms(m, s);
+  if (threadIdx.x == 0) p.stats[(static_cast<long>(b) * p.rows + r) * p.nch + c] = make_float2(m, s);
+}
+
+// With the chunk statistics given: clear the counters and gather the
+// drafts' logits. One thread per (sequence, verify row).
+template <typename E>
+__global__ __launch_bounds__(256) void accept_prep_kernel(AcceptParams p) {
+  const int nd = p.N - 1;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.C * nd) return;
+  const int b = i / nd, j = i % nd;
+  if (j == 0) p.arrive[b] = 0;
+  const int d = p.in.drafts[b * nd + j];
+  if (j < seq_n(p, b) && d >= 0 && d < p.V) p.lx[b * kMaxN + j] = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, j), d);
+}
+
+// ------------------------------------------------ per-sequence decision
+// Row statistics, uniforms and the accept decision of sequence b; every
+// workgroup of the decide launch computes the same values.
+struct Decision {
+  int n, a, err, qrow;
+  float2 ms[2 * kMaxN];                // row (max, sum)
+  float u[2 * kMaxN];                  // uniforms by slot
+  float px[kMaxN];                     // P_{j-1}(x_j) of tested drafts, NaN otherwise
+  float2 st[2 * kMaxN - 1][kMaxChunks];  // chunk statistics of the rows read
+};
+
+template <typename E>
+__device__ __forceinline__ void decide(const AcceptParams& p, int b, Decision& d) {
+  const int tid = threadIdx.x, N = p.N, nd = N - 1, R = 2 * N - 1, nch = p.nch;
+  __shared__ int s_nraw, s_draft[kMaxN];
+  __shared__ float s_qx[kMaxN], s_lx[kMaxN];
+  // everything in one round trip: the statistics of every row the step may
+  // read (those past n+N-1 are not used), the state, the drafts' logits
+  for (int i = tid; i < R * nch; i += kThreads)
+    d.st[i / nch][i % nch] = p.stats[(static_cast<long>(b) * p.rows + i / nch) * nch + i % nch];
+  if (tid == kThreads - 1) {
+    s_nraw = p.in.n_draft[b];
+    d.qrow = p.in.q_row[b];
   }
+  if (tid >= kThreads - 1 - kMaxN && tid < kThreads - 1 - kMaxN + nd) {
+    const int j = tid - (kThreads - 1 - kMaxN);
+    s_draft[j] = p.in.drafts[b * nd + j];
+    s_qx[j] = p.in.q_x[b * nd + j];
+    s_lx[j] = p.lx[b * kMaxN + j];
+  }
+  if (tid < 2 * N) d.u[tid] = slot_uniform(p, tid, b);
   __syncthreads();
-  if (a < n) {
-    // Residual: pick the chunk from the per-chunk sums, rescan it.
-    if (tid == 0) {
-      float W = 0.f;
-      for (int c = 0; c < p.nch; ++c) W += s_res[c];
-      s_mass = W;
-    }
-    __syncthreads();
-    const float W = s_mass;
-    int tok;
-    if (W > 0.f) {
-      const float t = d.u[N] * W;
-      __shared__ int s_c;
-      __shared__ float s_trel;
-      if (tid == 0) {
-        float run = 0.f;
-        int c_sel = -1, last_nz = 0;
-        float trel = INFINITY;
-        for (int c = 0; c < p.nch; ++c) {
-          const float wc = s_res[c];
-          if (wc > 0.f) last_nz = c;
-          if (c_sel < 0 && run + wc > t) {
-            c_sel = c;
-            trel = t - run;
-          }
-          run += wc;
-        }
-        s_c = c_sel >= 0 ? c_sel : last_nz;
-        s_trel = c_sel >= 0 ? trel : INFINITY;
-      }
-      __syncthreads();
-      float w[kPerThread];
-      resid_slice<E>(p, b, d, s_c, w);
-      tok = chunk_search(w, s_c, s_trel);
-    } else {
-      // No residual mass left (P_a <= Q_{a+1} everywhere): draw from P_a.
-      tok = sample_row<E>(p, d, b, a, d.u[N]);
-    }
-    if (tid == 0) s_t = tok;
-  } else {
-    if (tid == 0) s_t = s_smp[0].x;
-  }
+  const int n_raw = s_nraw;
+  const int n = (n_raw < 0 || n_raw > nd) ? 0 : n_raw;
+  if (tid < n + N) d.ms[tid] = row_ms(d.st[tid], nch);
   __syncthreads();
   if (tid == 0) {
-    const int t = s_t;
-    p.accepted[b] = a;
-    p.n_emit[b] = a + 1;
-    p.kv_commit[b] = a + 1;
-    if (p.ctx) p.ctx[b] += a + 1;
-    for (int k = 0; k < N; ++k) {
-      int v = -1;
-      if (k < a) v = p.in.drafts[b * nd + k];
-      if (k == a) v = t;
-      p.emit[b * N + k] = v;
-    }
-    if (a == n) {
-      p.out.n_draft[b] = nd;
-      p.out.q_row[b] = n + 1;
-      for (int k = 1; k <= nd; ++k) {
-        const int2 sp = s_smp[k];
-        p.out.drafts[b * nd + k - 1] = sp.x;
-        p.out.q_x[b * nd + k - 1] = __int_as_float(sp.y);
-        p.out.q_m[b * nd + k - 1] = d.M[n + k];
-        p.out.q_s[b * nd + k - 1] = d.S[n + k];
-      }
-    } else {
-      p.out.n_draft[b] = 0;
-      p.out.q_row[b] = 0;
-      for (int k = 0; k < nd; ++k) {
-        p.out.drafts[b * nd + k] = -1;
-        p.out.q_x[b * nd + k] = 0.f;
-        p.out.q_m[b * nd + k] = 0.f;
-        p.out.q_s[b * nd + k] = 0.f;
+    int err = 0;
+    if (n_raw < 0 || n_raw > nd) err |= ISD_DEV_STATE;
+    if (n > 0 && ((!p.argmax && !p.prev_logits) || d.qrow < 0 || d.qrow + n - 1 >= p.rows)) err |= ISD_DEV_STATE;
+    for (int j = 0; j < n; ++j)
+      if (s_draft[j] < 0 || s_draft[j] >= p.V) err |= ISD_DEV_TOKEN_OOB;
+    for (int r = 0; r < n + N; ++r)
+      if (!ms_finite(d.ms[r])) err |= ISD_DEV_NONFINITE;
+    int a = 0;
+    for (int j = 0; j < kMaxN; ++j) d.px[j] = NAN;
+    if (!err) {
+      for (int j = 1; j <= n; ++j) {
+        const float px = prob_of(s_lx[j - 1], d.ms[j - 1].x, d.ms[j - 1].y);
+        d.px[j - 1] = px;
+        // u * q < p compared exactly (fp32 operands, exact fp64 product).
+        if (static_cast<double>(d.u[j]) * static_cast<double>(s_qx[j - 1]) < static_cast<double>(px))
+          ++a;
+        else
+          break;
       }
     }
-    if (p.resid_mass) p.resid_mass[b] = (a < n) ? s_mass : -1.f;
-    if (p.p_x)
-      for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = d.px[k];
-    if (p.row_m)
-      for (int r = 0; r < p.rows; ++r) {
-        const bool rd = r < n + N;
-        p.row_m[b * p.rows + r] = rd ? d.M[r] : NAN;
-        p.row_s[b * p.rows + r] = rd ? d.S[r] : NAN;
-      }
+    d.n = n;
+    d.a = a;
+    d.err = err;
   }
+  __syncthreads();
 }
 
-// =========================================================== sample kernel
+// ================================================================ outputs
+// The outputs of sequence b that the decision alone fixes (all of them on
+// an error). What depends on a draw is written by the workgroup that makes
+// it: emit[a] (the bonus or the residual draw), the new drafts and their
+// q(x), the residual mass.
+__device__ __forceinline__ void write_decided(const AcceptParams& p, int b, const Decision& d) {
+  const int N = p.N, nd = N - 1, n = d.n, a = d.a;
+  if (d.err) {
+    p.accepted[b] = -1;
+    p.n_emit[b] = 0;
+    p.kv_commit[b] = 0;
+    for (int k = 0; k < N; ++k) p.emit[b * N + k] = -1;
+    p.out.n_draft[b] = p.in.n_draft[b];
+    p.out.q_row[b] = p.in.q_row[b];
+    for (int k = 0; k < nd; ++k) {
+      p.out.drafts[b * nd + k] = p.in.drafts[b * nd + k];
+      p.out.q_x[b * nd + k] = p.in.q_x[b * nd + k];
+      p.out.q_m[b * nd + k] = p.in.q_m[b * nd + k];
+      p.out.q_s[b * nd + k] = p.in.q_s[b * nd + k];
+    }
+    if (p.resid_mass) p.resid_mass[b] = -1.f;
+    if (p.p_x)
+      for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = NAN;
+    if (p.row_m)
+      for (int r = 0; r < p.rows; ++r) {
+        p.row_m[b * p.rows + r] = NAN;
+        p.row_s[b * p.rows + r] = NAN;
+      }
+    set_dev_err(p.dev_err, static_cast<uint32_t>(d.err));
+    return;
+  }
+  p.accepted[b] = a;
+  p.n_emit[b] = a + 1;
+  p.kv_commit[b] = a + 1;
+  if (p.ctx) p.ctx[b] += a + 1;
+  for (int k = 0; k < N; ++k)
+    if (k != a) p.emit[b * N + k] = k < a ? p.in.drafts[b * nd + k] : -1;
+  if (a == n) {
+    p.out.n_draft[b] = nd;
+    p.out.q_row[b] = n + 1;
+    for (int k = 1; k <= nd; ++k) {
+      p.out.q_m[b * nd + k - 1] = d.ms[n + k].x;
+      p.out.q_s[b * nd + k - 1] = d.ms[n + k].y;
+    }
+    if (p.resid_mass) p.resid_mass[b] = -1.f;
+  } else {
+    p.out.n_draft[b] = 0;
+    p.out.q_row[b] = 0;
+    for (int k = 0; k < nd; ++k) {
+      p.out.drafts[b * nd + k] = -1;
+      p.out.q_x[b * nd + k] = 0.f;
+      p.out.q_m[b * nd + k] = 0.f;
+      p.out.q_s[b * nd + k] = 0.f;
+    }
+  }
+  if (p.p_x)
+    for (int k = 0; k < nd; ++k) p.p_x[b * nd + k] = d.px[k];
+  if (p.row_m)
+    for (int r = 0; r < p.rows; ++r) {
+      const bool rd = r < n + N;
+      p.row_m[b * p.rows + r] = rd ? d.ms[r].x : NAN;
+      p.row_s[b * p.rows + r] = rd ? d.ms[r].y : NAN;
+    }
+}
+
+// =========================================================== decide kernel
 template <typename E>
-__global__ __launch_bounds__(kThreads) void accept_sample_kernel(AcceptParams p) {
-  const int slice = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kThreads) void accept_decide_kernel(AcceptParams p) {
+  const int slice = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ Decision d;
   decide<E>(p, b, d);
-  const int n = d.n, a = d.a;
-  if (!d.err) {
-    if (a < n) {
-      // residual sums of chunks kStatsChunks * slice ..
-#pragma unroll
-      for (int h = 0; h < kStatsChunks; ++h) {
-        const int c = kStatsChunks * slice + h;
-        if (c < p.nch) {
-          float w[kPerThread];
-          resid_slice<E>(p, b, d, c, w);
-          float local = 0.f;
-#pragma unroll
-          for (int k = 0; k < kPerThread; ++k) local += w[k];
-          const float tot = block_sum(local);
-          if (threadIdx.x == 0) put_f32(&p.resid[static_cast<long>(b) * p.nch + c], tot);
-        }
-      }
-    } else if (slice < p.N) {
-      const int r = n + slice;  // slice 0: bonus row n; slice k: proposal row n + k
-      if (p.argmax && slice > 0) {
-        const int tok = argmax_row<E>(p, d, b, r);
-        if (threadIdx.x == 0) put_sample(&p.samp[b * p.N + slice], tok, 1.f);
+  const int n = d.n, a = d.a, N = p.N, nd = N - 1;
+  if (slice == 0 && tid == 0) write_decided(p, b, d);
+  if (d.err) return;
+  const int nres = (p.nch + kResidChunks - 1) / kResidChunks;  // residual slices
+  if (slice >= (a == n ? N : nres)) return;
+  if (a == n) {
+    // Every draft passed. Slice 0 draws the bonus from row n, slice k
+    // proposal k from row n + k; each writes its own outputs.
+    const int r = n + slice;
+    int tok;
+    float q;
+    if (p.argmax && slice > 0) {
+      tok = argmax_row<E>(p, b, r, d.st[r], d.ms[r].x);
+      q = 1.f;
+    } else {
+      tok = sample_row<E>(p, b, r, d.st[r], d.ms[r].x, d.ms[r].y, d.u[N + slice], &q);
+    }
+    if (tid == 0) {
+      if (slice == 0) {
+        p.emit[b * N + a] = tok;
       } else {
-        const int tok = sample_row<E>(p, d, b, r, d.u[p.N + slice]);
-        if (threadIdx.x == 0) {
-          const float l = load_elem(row_ptr<E>(p.logits, p.ld, p.rows, b, r), tok);
-          put_sample(&p.samp[b * p.N + slice], tok, prob_of(l, d.M[r], d.S[r]));
-        }
+        p.out.drafts[b * nd + slice - 1] = tok;
+        p.out.q_x[b * nd + slice - 1] = q;
+      }
+    }
+    return;
+  }
+  // Draft a+1 was rejected: residual sums of chunks kResidChunks * slice ..
+  __shared__ ResidArgs s_ra;
+  if (tid == 0) {
+    ResidArgs ra;
+    ra.a = a;
+    ra.Ma = d.ms[a].x;
+    ra.Sa = d.ms[a].y;
+    ra.qm = p.in.q_m[b * nd + a];
+    ra.qs = p.in.q_s[b * nd + a];
+    ra.qrow = d.qrow;
+    ra.x_rej = p.in.drafts[b * nd + a];
+    s_ra = ra;
+  }
+  __syncthreads();
+  {
+    const ResidArgs ra = s_ra;
+    ResidWeights<E> wf[kResidChunks];
+#pragma unroll
+    for (int h = 0; h < kResidChunks; ++h) {
+      const int c = kResidChunks * slice + h;
+      if (c < p.nch) wf[h] = resid_weights<E>(p, b, ra, c);  // both chunks' loads in flight together
+    }
+#pragma unroll
+    for (int h = 0; h < kResidChunks; ++h) {
+      const int c = kResidChunks * slice + h;
+      if (c < p.nch) {
+        float local = 0.f;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) local += wf[h](k);
+        const float tot = block_sum(local);
+        if (tid == 0) put_f32(&p.resid[static_cast<long>(b) * p.nch + c], tot);
       }
     }
   }
   // Arrival: thread 0 made this workgroup's stores; once they are complete
-  // (vmcnt 0) it counts the workgroup in. The one that brings the count to
-  // ns reads everybody's results with device-coherent loads.
+  // it counts the workgroup in. The one that brings the count to nres
+  // reads every slice's sums with device-coherent loads, picks the chunk
+  // and rescans it.
   __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    // the compiler may not move the slice stores past the wait, nor the
-    // counter update above it; the wait makes the stores complete first
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");
-    s_last = __hip_atomic_fetch_add(&p.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.ns - 1;
+  if (tid == 0) {
+    stores_done();
+    s_last = __hip_atomic_fetch_add(&p.arrive[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nres - 1;
     asm volatile("" ::: "memory");
   }
   __syncthreads();
   if (!s_last) return;
-  finish<E>(p, b, d);
+  __shared__ float s_res[kMaxChunks];
+  __shared__ float s_mass, s_trel;
+  __shared__ int s_c;
+  if (tid < p.nch) s_res[tid] = get_f32(&p.resid[static_cast<long>(b) * p.nch + tid]);
+  __syncthreads();
+  if (tid == 0) {
+    float W = 0.f;
+    for (int c = 0; c < p.nch; ++c) W += s_res[c];
+    s_mass = W;
+    const float t = d.u[N] * W;
+    float run = 0.f, trel = INFINITY;
+    int c_sel = -1, last_nz = 0;
+    for (int c = 0; c < p.nch; ++c) {
+      const float wc = s_res[c];
+      if (wc > 0.f) last_nz = c;
+      if (c_sel < 0 && run + wc > t) {
+        c_sel = c;
+        trel = t - run;
+      }
+      run += wc;
+    }
+    s_c = c_sel >= 0 ? c_sel : last_nz;
+    s_trel = c_sel >= 0 ? trel : INFINITY;
+  }
+  __syncthreads();
+  int tok;
+  if (s_mass > 0.f) {
+    ResidWeights<E> wf = resid_weights<E>(p, b, s_ra, s_c);
+    float w;
+    tok = chunk_search(wf, s_c, s_trel, &w);
+  } else {
+    // No residual mass left (P_a <= Q_{a+1} everywhere): draw from P_a.
+    float q;
+    tok = sample_row<E>(p, b, a, d.st[a], d.ms[a].x, d.ms[a].y, d.u[N], &q);
+  }
+  if (tid == 0) {
+    p.emit[b * N + a] = tok;
+    if (p.resid_mass) p.resid_mass[b] = s_mass;
+  }
 }
 
 // ----------------------------------------------------------- block assembly
@@ -706,35 +802,37 @@ using namespace isd;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+size_t up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 struct AcceptLayout {
   int nch, ns;
-  size_t stats_off, resid_off, samp_off, arrive_off, total;
+  size_t stats_off, lx_off, resid_off, arrive_off, total;
 };
 
 AcceptLayout accept_layout(int C, int N, int V, int rows) {
   AcceptLayout L;
   L.nch = (V + kChunk - 1) / kChunk;
-  const int pairs = (L.nch + kStatsChunks - 1) / kStatsChunks;
-  L.ns = pairs > N ? pairs : N;
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const int nres = (L.nch + kResidChunks - 1) / kResidChunks;
+  L.ns = nres > N ? nres : N;
   L.stats_off = 0;
-  L.resid_off = up(static_cast<size_t>(C) * rows * L.nch * sizeof(float2));
-  L.samp_off = L.resid_off + up(static_cast<size_t>(C) * L.nch * sizeof(float));
-  L.arrive_off = L.samp_off + up(static_cast<size_t>(C) * N * sizeof(int2));
-  L.total = L.arrive_off + up(static_cast<size_t>(C) * sizeof(int));
+  L.lx_off = up256(static_cast<size_t>(C) * rows * L.nch * sizeof(float2));
+  L.resid_off = L.lx_off + up256(static_cast<size_t>(C) * kMaxN * sizeof(float));
+  L.arrive_off = L.resid_off + up256(static_cast<size_t>(C) * L.nch * sizeof(float));
+  L.total = L.arrive_off + up256(static_cast<size_t>(C) * sizeof(int));
   return L;
 }
 
 bool state_ok(const isd_seq_state& s) { return s.n_draft && s.drafts && s.q_x && s.q_m && s.q_s && s.q_row; }
 
 template <typename E>
-hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
-  if (p.stats_given)
-    hipLaunchKernelGGL(accept_arrive_reset_kernel, dim3((p.C + 255) / 256), dim3(256), 0, stream, p.arrive, p.C);
-  else
-    hipLaunchKernelGGL(accept_stats_kernel<E>, dim3((p.nch + kStatsChunks - 1) / kStatsChunks, 2 * p.N - 1, p.C),
-                       dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(accept_sample_kernel<E>, dim3(p.ns, p.C), dim3(kThreads), 0, stream, p);
+hipError_t launch_accept(const AcceptParams& p, bool stats_given, hipStream_t stream) {
+  if (stats_given) {
+    const int threads = p.C * (p.N - 1);
+    hipLaunchKernelGGL(accept_prep_kernel<E>, dim3((threads + 255) / 256), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(accept_stats_kernel<E>, dim3(p.nch, 2 * p.N - 1, p.C), dim3(kThreads), 0, stream, p);
+  }
+  hipLaunchKernelGGL(accept_decide_kernel<E>, dim3(p.ns, p.C), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -797,15 +895,16 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.row_m = a->row_m;
   p.row_s = a->row_s;
   char* ws = static_cast<char*>(a->ws);
-  p.stats_given = a->chunk_stats != nullptr;
-  p.stats = p.stats_given ? reinterpret_cast<float2*>(const_cast<float*>(a->chunk_stats))
-                          : reinterpret_cast<float2*>(ws + L.stats_off);
+  const bool given = a->chunk_stats != nullptr;
+  p.stats = given ? reinterpret_cast<float2*>(const_cast<float*>(a->chunk_stats))
+                  : reinterpret_cast<float2*>(ws + L.stats_off);
+  p.lx = reinterpret_cast<float*>(ws + L.lx_off);
   p.resid = reinterpret_cast<float*>(ws + L.resid_off);
-  p.samp = reinterpret_cast<int2*>(ws + L.samp_off);
   p.arrive = reinterpret_cast<int*>(ws + L.arrive_off);
   p.argmax = a->proposal == ISD_PROPOSE_ARGMAX;
   p.dev_err = a->dev_err;
-  const hipError_t e = a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, stream) : launch_accept<float>(p, stream);
+  const hipError_t e =
+      a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, given, stream) : launch_accept<float>(p, given, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 

@@ -342,7 +342,7 @@ def test_stride_sweep_tokens_per_forward(N, p):
     ctx0 = torch.full((C,), 16384, dtype=torch.int64, device=DEV)
     ctx = ctx0.clone()
     s_in, s_out = dvd.SeqState(C, N), dvd.SeqState(C, N)
-    ws = torch.empty(dvd.isd_accept_workspace_size(C, N, V, 2 * N), dtype=torch.uint8, device=DEV)
+    ws = dvd.accept_workspace(C, N, V, 2 * N, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     prev = None
     tokens = torch.zeros(C, dtype=torch.int64, device=DEV)
@@ -470,7 +470,7 @@ def test_graph_replay_of_the_device_step_matches_eager():
     def side():
         st = [dvd.SeqState(C, N), dvd.SeqState(C, N)]
         return dict(st=st, ctx=ctx0.to(torch.int32).clone(), out=dvd.AcceptOutputs(C, N, R, DEV, diag=False),
-                    ws=torch.empty(dvd.isd_accept_workspace_size(C, N, V, R), dtype=torch.uint8, device=DEV),
+                    ws=dvd.accept_workspace(C, N, V, R, device=DEV),
                     err=torch.zeros(1, dtype=torch.int32, device=DEV),
                     tok=torch.empty((C, R), dtype=torch.int32, device=DEV),
                     pos=torch.empty((C, R), dtype=torch.int32, device=DEV),
