@@ -98,6 +98,8 @@ _SIGNATURES = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "isd_accept_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "isd_accept": (ctypes.c_int, [ctypes.POINTER(IsdAcceptArgs), ctypes.c_void_p]),
+    "isd_accept_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "isd_accept_noalloc": (ctypes.c_int, [ctypes.POINTER(IsdAcceptArgs), ctypes.c_void_p]),
     "isd_block_assemble": (ctypes.c_int, [ctypes.POINTER(IsdSeqState), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -304,19 +306,21 @@ class AcceptOutputs:
 
 def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, out=None, ws=None,
                diag=False, dev_err=None, ctx=None, stream=None, proposal="sample", step_dev=None,
-               chunk_stats=None):
+               chunk_stats=None, noalloc=False):
     """One accept step. logits [C, rows, ld] (bf16 or fp32); returns the
     AcceptOutputs (device tensors) and writes state_out. If ctx (int32 [C])
     is given, the kernel adds kv_commit to it. proposal: "sample" or
     "argmax" (drafts = argmax of the MASK rows). step_dev: optional int64
     device tensor [1] holding the step number (then `step` is ignored), for
     calls captured in a graph. chunk_stats: optional fp32 [C, rows, nch, 2]
-    from isd_lm_head (then the statistics pass is skipped)."""
+    from isd_lm_head (then the statistics pass is skipped). noalloc: call
+    isd_accept_noalloc, whose workspace is the library's fixed device array
+    (ws is then ignored and none is allocated)."""
     C, rows, ld = logits.shape
     V = ld if V is None else V
     if out is None:
         out = AcceptOutputs(C, N, rows, logits.device, diag)
-    if ws is None:
+    if ws is None and not noalloc:
         ws = accept_workspace(C, N, V, rows, logits.device)
     args = IsdAcceptArgs()
     args.C, args.N, args.V, args.rows = C, N, V, rows
@@ -333,13 +337,16 @@ def isd_accept(logits, prev_logits, state_in, state_out, N, seed, step, V=None, 
     for name in ("p_x", "resid_mass", "row_m", "row_s"):
         t = getattr(out, name)
         setattr(args, name, None if t is None else t.data_ptr())
-    args.ws = ws.data_ptr()
-    args.ws_bytes = ws.numel() * ws.element_size()
+    args.ws = None if ws is None else ws.data_ptr()
+    args.ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     args.dev_err = None if dev_err is None else dev_err.data_ptr()
     args.proposal = PROPOSE[proposal]
     args.step_dev = None if step_dev is None else step_dev.data_ptr()
     args.chunk_stats = None if chunk_stats is None else chunk_stats.data_ptr()
-    _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
+    if noalloc:
+        _check(lib().isd_accept_noalloc(ctypes.byref(args), _stream(stream)), "isd_accept_noalloc")
+    else:
+        _check(lib().isd_accept(ctypes.byref(args), _stream(stream)), "isd_accept")
     return out
 
 

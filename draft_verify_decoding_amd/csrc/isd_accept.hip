@@ -32,6 +32,8 @@
 // When the caller passes the chunk statistics (isd_lm_head wrote them with
 // the logits), a small launch that clears the counters and gathers the
 // drafts' logits replaces the stats launch.
+#include <mutex>
+
 #include "isd_common.hpp"
 
 namespace isd {
@@ -796,6 +798,13 @@ __global__ __launch_bounds__(256) void block_assemble_kernel(const int32_t* n_dr
 
 }  // namespace isd
 
+// The workspace of isd_accept_noalloc: a fixed array in device memory, one
+// copy per GPU, kept until the process ends. In host code its name is only a
+// stand-in: the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 // ================================================================ host API
 namespace {
 using namespace isd;
@@ -845,7 +854,12 @@ size_t isd_accept_workspace_size(int C, int N, int V, int rows) {
   return accept_layout(C, N, V, rows).total;
 }
 
-int isd_accept(const isd_accept_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// isd_accept with the workspace given separately (ws_bytes 0: none).
+int accept_with_workspace(const isd_accept_args* a, void* ws_ptr, size_t ws_bytes, hipStream_t stream) {
   if (!a) return ISD_E_INVALID;
   if (a->C < 0 || a->N < 2 || a->V < 1) return ISD_E_INVALID;
   if (a->C > 65535) return ISD_E_UNSUPPORTED;  // sequences map to a grid dimension
@@ -866,7 +880,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
       a->in.q_m == a->out.q_m || a->in.q_s == a->out.q_s || a->in.q_row == a->out.q_row)
     return ISD_E_INVALID;
   const AcceptLayout L = accept_layout(a->C, a->N, a->V, a->rows);
-  if (!a->ws || a->ws_bytes < L.total || !aligned16(a->ws)) return ISD_E_WORKSPACE;
+  if (!ws_ptr || ws_bytes < L.total || !aligned16(ws_ptr)) return ISD_E_WORKSPACE;
   int rc = isd_check_device_internal();
   if (rc) return rc;
 
@@ -894,7 +908,7 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   p.resid_mass = a->resid_mass;
   p.row_m = a->row_m;
   p.row_s = a->row_s;
-  char* ws = static_cast<char*>(a->ws);
+  char* ws = static_cast<char*>(ws_ptr);
   const bool given = a->chunk_stats != nullptr;
   p.stats = given ? reinterpret_cast<float2*>(const_cast<float*>(a->chunk_stats))
                   : reinterpret_cast<float2*>(ws + L.stats_off);
@@ -906,6 +920,45 @@ int isd_accept(const isd_accept_args* a, hipStream_t stream) {
   const hipError_t e =
       a->dtype == ISD_BF16 ? launch_accept<uint16_t>(p, given, stream) : launch_accept<float>(p, given, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
+}
+
+// ------------------------------------------------- allocation-free variant
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device, or null.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int isd_accept(const isd_accept_args* a, hipStream_t stream) {
+  if (!a) return ISD_E_INVALID;
+  return accept_with_workspace(a, a->ws, a->ws_bytes, stream);
+}
+
+size_t isd_accept_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+int isd_accept_noalloc(const isd_accept_args* a, hipStream_t stream) {
+  if (!a) return ISD_E_INVALID;
+  const size_t need = isd_accept_workspace_size(a->C, a->N, a->V, a->rows);
+  if (need > kNoAllocScratchBytes) return ISD_E_WORKSPACE;  // beyond the fixed scratch
+  const int rc = isd_check_device_internal();
+  if (rc) return rc;
+  void* ws = scratch_address();
+  if (!ws) return ISD_E_LAUNCH;
+  return accept_with_workspace(a, ws, kNoAllocScratchBytes, stream);
 }
 
 int isd_block_assemble(const isd_seq_state* st, const int32_t* emit, const int32_t* n_emit, const int32_t* ctx,

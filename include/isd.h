@@ -279,6 +279,20 @@ typedef struct isd_accept_args {
 size_t isd_accept_workspace_size(int C, int N, int V, int rows);
 int isd_accept(const isd_accept_args* args, hipStream_t stream);
 
+/* isd_accept_noalloc: isd_accept for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). args->ws and args->ws_bytes are ignored: the workspace
+ * is a fixed array in the library's device memory, one per GPU, of
+ * isd_accept_noalloc_max_workspace() bytes (4 MiB), kept until the process
+ * ends. The call allocates nothing. A call whose
+ * isd_accept_workspace_size(C, N, V, rows) exceeds that maximum returns
+ * ISD_E_WORKSPACE without launching. Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. Results are those of isd_accept on
+ * the same arguments. */
+size_t isd_accept_noalloc_max_workspace(void);
+int isd_accept_noalloc(const isd_accept_args* args, hipStream_t stream);
+
 /* Block assembly: the stride block of the next step, from the state and
  * outputs isd_accept just wrote (I-DLM page, "Methodologie d'I-DLM >
  * Introspective Strided Decoding (ISD)": one forward carries the clean

@@ -42,6 +42,11 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(handle, name), name
 
 
+def test_noalloc_accept_rejects_a_null_argument_on_host(lib):
+    assert lib.isd_accept_noalloc(None, None) == -1
+    assert lib.isd_accept_noalloc_max_workspace() == 4 << 20
+
+
 def test_strerror_and_version(lib):
     assert dvd.strerror(0) == "success"
     for code in (-1, -2, -3, -4, -5):
