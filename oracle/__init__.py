@@ -11,6 +11,8 @@ share no code. Modules:
   accept    softmax, inverse CDF, the verify / resample / propose step
   lora      base projection and gated LoRA
   chain     the tokens-per-forward closed form and its two-state chain
+  forward   RMSNorm, SwiGLU, bf16 rounding and a decoder block built
+            from the modules above
 """
 
-from . import accept, attention, chain, lora, philox  # noqa: F401
+from . import accept, attention, chain, forward, lora, philox  # noqa: F401
