@@ -114,6 +114,11 @@ _SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "isd_rmsnorm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
+    "isd_cast_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
+    "isd_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "isd_lm_head_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int]),
     "isd_lm_head": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -438,6 +443,37 @@ def prepare_lm_head(h, W, logits, chunk_stats, ws, stream=None):
                     ws.numel() * ws.element_size(), _stream(stream), keep=(h, W, logits, chunk_stats, ws))
 
 
+# ---------------------------------------------------------- decoder block
+def isd_rmsnorm(h, gamma, out=None, delta=None, eps=1e-6, stream=None):
+    """h [M, H] fp32 (updated in place with h += delta when delta is given);
+    returns out [M, H] bf16 = rmsnorm(h) * gamma."""
+    M, H = h.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
+    _check(lib().isd_rmsnorm(_p(h), _p(delta), _p(gamma), M, H, float(eps), _p(out), _stream(stream)), "isd_rmsnorm")
+    return out
+
+
+def isd_cast_bf16(src, outs, stream=None):
+    """Columns of src [M, ld] fp32 split into the bf16 tensors outs (each
+    [M, w] contiguous, or any tensor of M * w elements), in order."""
+    M, ld = src.shape[0], src.stride(0)
+    widths = [o.numel() // M for o in outs]
+    w_arr = (ctypes.c_int * len(outs))(*widths)
+    d_arr = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    _check(lib().isd_cast_bf16(_p(src), ld, M, len(outs), w_arr, d_arr, _stream(stream)), "isd_cast_bf16")
+    return outs
+
+
+def isd_swiglu(gu, out=None, stream=None):
+    """gu [M, 2I] fp32 (gate | up) -> out [M, I] bf16 = silu(gate) * up."""
+    M, I2 = gu.shape
+    if out is None:
+        out = torch.empty((M, I2 // 2), dtype=torch.bfloat16, device=gu.device)
+    _check(lib().isd_swiglu(_p(gu), M, I2 // 2, _p(out), _stream(stream)), "isd_swiglu")
+    return out
+
+
 # ------------------------------------------------------- prepared calls
 class Prepared:
     """One library call with its arguments marshalled once, for loops that
@@ -494,3 +530,62 @@ def prepare_linear_gated(x, W, A, B, is_mask, y, ws, scale=1.0, stream=None):
     return Prepared("isd_linear_gated", _p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, W.shape[0], A.shape[0],
                     float(scale), _p(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream),
                     keep=(x, W, A, B, is_mask, y, ws))
+
+
+def prepare_rmsnorm(h, gamma, out, delta=None, eps=1e-6, stream=None):
+    M, H = h.shape
+    return Prepared("isd_rmsnorm", _p(h), _p(delta), _p(gamma), M, H, float(eps), _p(out), _stream(stream),
+                    keep=(h, gamma, out, delta))
+
+
+def prepare_cast_bf16(src, outs, stream=None):
+    M, ld = src.shape[0], src.stride(0)
+    w_arr = (ctypes.c_int * len(outs))(*[o.numel() // M for o in outs])
+    d_arr = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    return Prepared("isd_cast_bf16", _p(src), ld, M, len(outs), w_arr, d_arr, _stream(stream),
+                    keep=(src, tuple(outs), w_arr, d_arr))
+
+
+def prepare_swiglu(gu, out, stream=None):
+    M, I2 = gu.shape
+    return Prepared("isd_swiglu", _p(gu), M, I2 // 2, _p(out), _stream(stream), keep=(gu, out))
+
+
+def prepare_accept(logits, prev_logits, state_in, state_out, N, seed, out, ws, V=None, ctx=None, dev_err=None,
+                   proposal="sample", step_dev=None, chunk_stats=None, stream=None):
+    """isd_accept with its arguments marshalled once; the returned call takes
+    the step number."""
+    C, rows, ld = logits.shape
+    args = IsdAcceptArgs()
+    args.C, args.N, args.V, args.rows = C, N, ld if V is None else V, rows
+    args.dtype = _dtype_code(logits)
+    args.logits = logits.data_ptr()
+    args.prev_logits = None if prev_logits is None else prev_logits.data_ptr()
+    args.ld = ld
+    args.in_ = state_in.c_struct()
+    args.out = state_out.c_struct()
+    args.seed = int(seed)
+    args.accepted, args.n_emit = out.accepted.data_ptr(), out.n_emit.data_ptr()
+    args.emit, args.kv_commit = out.emit.data_ptr(), out.kv_commit.data_ptr()
+    args.ctx = None if ctx is None else ctx.data_ptr()
+    for name in ("p_x", "resid_mass", "row_m", "row_s"):
+        t = getattr(out, name)
+        setattr(args, name, None if t is None else t.data_ptr())
+    args.ws = ws.data_ptr()
+    args.ws_bytes = ws.numel() * ws.element_size()
+    args.dev_err = None if dev_err is None else dev_err.data_ptr()
+    args.proposal = PROPOSE[proposal]
+    args.step_dev = None if step_dev is None else step_dev.data_ptr()
+    args.chunk_stats = None if chunk_stats is None else chunk_stats.data_ptr()
+    fn = lib().isd_accept
+    stream_p = _stream(stream)
+    keep = (logits, prev_logits, state_in, state_out, out, ws, ctx, dev_err, step_dev, chunk_stats)
+
+    def call(step):
+        args.step = int(step)
+        rc = fn(ctypes.byref(args), stream_p)
+        if rc != 0:
+            raise IsdError(rc, "isd_accept")
+    call.keep = keep
+    call.args = args
+    return call

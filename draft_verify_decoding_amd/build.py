@@ -6,7 +6,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["isd_runtime.hip", "isd_attention.hip", "isd_accept.hip", "isd_linear.hip"]
+SOURCES = ["isd_runtime.hip", "isd_attention.hip", "isd_accept.hip", "isd_linear.hip", "isd_forward.hip"]
 LIB = os.path.join(HERE, "libisd.so")
 
 FLAGS = [

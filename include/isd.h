@@ -19,6 +19,9 @@
  *   gated_lora_apply  y += s (x A^T) B^T on MASK rows only (R-ISD)
  *   isd_linear_gated  both of the above in one pass
  *   isd_lm_head       logits = h W^T (bf16) with their softmax chunk statistics
+ *   isd_rmsnorm, isd_cast_bf16, isd_swiglu
+ *                     the normalisation, cast and activation steps of the
+ *                     decoder block around them
  *
  * Conventions shared by every call:
  *   - Every pointer argument is device memory owned by the caller, except
@@ -385,6 +388,40 @@ size_t isd_lm_head_workspace_size(int M, int V);
 int isd_lm_head(const void* h, const void* W, int M, int K, int V,
                 void* logits, int64_t ld, float* chunk_stats, void* ws,
                 size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------- the decoder block
+ * One ISD step is one causal forward of the model (I-DLM page,
+ * "Methodologie d'I-DLM"); the released models are built on Qwen3-8B and
+ * Qwen3-32B ("Documentation et ressources > Model Zoo"). The pages do not
+ * describe the block; these calls are the pieces of the usual pre-norm
+ * block of that family (RMSNorm, SwiGLU MLP) that the projections,
+ * attention and LM head above do not cover, so that a whole forward runs
+ * in this library. Each streams its operands once.
+ *
+ * isd_rmsnorm: for every row m of h [M][H] (fp32, the residual stream),
+ *   h[m] += delta[m] when delta [M][H] is not NULL (the residual add, in
+ *   place), then out[m] = bf16(h[m] / sqrt(mean(h[m]^2) + eps) * gamma)
+ *   with gamma [H] bf16 and out [M][H] bf16 (round to nearest even). The
+ *   mean square is summed in a fixed order per row. H a multiple of 4;
+ *   h, delta 16-byte aligned, gamma, out 8-byte aligned.
+ * isd_cast_bf16: splits the columns of src [M][ld] fp32 into nparts
+ *   (1..4) consecutive ranges of widths[p] columns (host array, each a
+ *   multiple of 4) and writes range p, rounded to bf16, to dst[p] (host
+ *   array of device pointers, each [M][widths[p]] contiguous, 8-byte
+ *   aligned): e.g. a fused Q|K|V projection into q, k and v. ld >= the sum
+ *   of the widths and a multiple of 4; src 16-byte aligned.
+ * isd_swiglu: out[m][i] = bf16(silu(gu[m][i]) * gu[m][I + i]),
+ *   silu(z) = z / (1 + exp(-z)), for gu [M][2I] fp32 (the gate columns,
+ *   then the up columns, of one fused projection) and out [M][I] bf16.
+ *   I a multiple of 4; gu 16-byte, out 8-byte aligned.
+ * Errors: ISD_E_INVALID (null or misaligned pointer, bad size),
+ * ISD_E_UNSUPPORTED (H not a multiple of 4); M == 0 launches nothing.
+ */
+int isd_rmsnorm(float* h, const float* delta, const void* gamma, int M, int H,
+                float eps, void* out, hipStream_t stream);
+int isd_cast_bf16(const float* src, int64_t ld, int M, int nparts,
+                  const int* widths, void* const* dst, hipStream_t stream);
+int isd_swiglu(const float* gu, int M, int I, void* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }
