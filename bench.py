@@ -43,9 +43,9 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 PROBE_EVERY = 8  # timed steps between the ones bracketed with HIP events
 
-CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, lora_rank=32,
+CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, intermediate=12288, lora_rank=32,
            ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3, proposal="sample")
-CFG_32B = dict(CFG, C=16, Hq=64, Hkv=8, D=128, layers=64, hidden=5120, ctx=16384)
+CFG_32B = dict(CFG, C=16, Hq=64, Hkv=8, D=128, layers=64, hidden=5120, intermediate=25600, ctx=16384)
 
 
 def log(*a):
@@ -285,6 +285,125 @@ def lm_head_leg(cfg, dev, calls=20):
     return res
 
 
+def forward_leg(cfg, st, dev, slices, steps=6, warmup=2):
+    """The whole synthetic forward of the step, chained through its real
+    outputs: for every layer RMSNorm, gated Q|K|V projection, bf16 q/k/v,
+    attention of the block over the pages, gated O projection, residual add
+    and RMSNorm, gate|up projection, SwiGLU, down projection; then the final
+    norm, the LM head (logits and their chunk statistics), isd_accept on
+    those statistics, the KV commit of the accepted rows and the next
+    block's assembly. Random weights of the 8B-class shapes (intermediate
+    12288); the block's embeddings are a fixed random input. Timed with the
+    adapters at rank 32 (stacked on the fused Q|K|V) and at rank 128 (one
+    per projection, Q, K and V then run as three projections), each against
+    the same forward with the base projections only: alpha is the ratio of
+    the step times (the pages quote 1.12 at rank 128)."""
+    import draft_verify_decoding_amd as dvd
+    import workload
+    from draft_verify_decoding_amd import forward as fwd
+
+    C, N, Hq, Hkv, D, L, V, H = (cfg[k] for k in ("C", "N", "Hq", "Hkv", "D", "layers", "V", "hidden"))
+    I = cfg["intermediate"]
+    R, M, seed = 2 * N, cfg["C"] * 2 * cfg["N"], cfg["seed"]
+    nq = (Hq + 2 * Hkv) * D
+    nrm = lambda shape, std, *tag: workload.normal(shape, std, torch.bfloat16, dev, seed, "fwd", *tag)
+    ones = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    t0 = time.perf_counter()
+    base = [dict(Wqkv=nrm((nq, H), 0.02, "Wqkv", l), Wo=nrm((H, Hq * D), 0.02, "Wo", l),
+                 Wgu=nrm((2 * I, H), 0.02, "Wgu", l), Wd=nrm((H, I), 0.02, "Wd", l)) for l in range(L)]
+
+    def stacked(l, r):
+        A = nrm((3 * r, H), 0.01, "Aqkv", r, l)
+        B = torch.zeros((nq, 3 * r), dtype=torch.bfloat16, device=dev)
+        off = 0
+        for i, w in enumerate((Hq * D, Hkv * D, Hkv * D)):
+            B[off:off + w, i * r:(i + 1) * r] = nrm((w, r), 0.01, "Bqkv", r, i, l)
+            off += w
+        return A, B
+
+    def layers(r, split):
+        out = []
+        for l, b in enumerate(base):
+            kw = dict(Ao=nrm((r, Hq * D), 0.01, "Ao", r, l), Bo=nrm((H, r), 0.01, "Bo", r, l))
+            if split:
+                kw["qkv_adapters"] = [(nrm((r, H), 0.01, "Aq", r, i, l), nrm((w, r), 0.01, "Bq", r, i, l))
+                                      for i, w in enumerate((Hq * D, Hkv * D, Hkv * D))]
+            else:
+                kw["Aqkv"], kw["Bqkv"] = stacked(l, r)
+            out.append(fwd.LayerWeights(ones, ones, b["Wqkv"], b["Wo"], b["Wgu"], b["Wd"], **kw))
+        return out
+
+    Wlm = nrm((V, H), 3.0 / H ** 0.5, "Wlm")
+    h0 = workload.normal((M, H), 1.0, torch.float32, dev, seed, "fwd-h0")
+    mask = st["mask"]
+    ctx0 = torch.from_numpy(st["ctx0"].astype(np.int32)).to(dev)
+    max_len = int(st["ctx0"].max()) + R + (steps + warmup + 1) * N
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    log(f"[bench] forward leg: weights built in {time.perf_counter() - t0:.1f} s")
+
+    def run(lw, lora):
+        ctx = ctx0.clone()
+        ctx_prev = torch.empty_like(ctx)
+        fw = fwd.Forward(lw, st["kvs"], ctx, mask, ones, Wlm, C, N, Hq, Hkv, D, max_len, slices, st["k_all"],
+                         st["v_all"], lora=lora, dev_err=err, dev=dev)
+        s = [dvd.SeqState(C, N, dev), dvd.SeqState(C, N, dev)]
+        out = dvd.AcceptOutputs(C, N, R, dev, diag=False)
+        ws = dvd.accept_workspace(C, N, V, R, device=dev)
+        acc = [dvd.prepare_accept(fw.logits_buf[par], fw.logits_buf[1 - par], s[par], s[1 - par], N, seed, out, ws,
+                                  ctx=ctx, dev_err=err, chunk_stats=fw.stats) for par in (0, 1)]
+        commit = dvd.prepare_kv_write_layers(st["kvs"][0], st["layer_stride"], st["k_all"], st["v_all"], ctx_prev,
+                                             out.kv_commit, dev_err=err)
+        tok = torch.empty((C, R), dtype=torch.int32, device=dev)
+        tokens = 0
+
+        def one(t):
+            par = t % 2
+            ctx_prev.copy_(ctx)
+            fw(h0, par)
+            acc[par](t)
+            commit()
+            dvd.isd_block_assemble(s[1 - par], out.emit, out.n_emit, ctx, N, V, tokens=tok, dev_err=err)
+
+        for t in range(warmup):
+            one(t)
+        torch.cuda.synchronize()
+        c0 = ctx.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warmup, warmup + steps):
+            one(t)
+        e1.record()
+        torch.cuda.synchronize()
+        assert err.item() == 0, f"device error flags {err.item()}"
+        tokens = int((ctx - c0).sum())
+        ms = e0.elapsed_time(e1) / steps
+        del fw, acc, commit
+        return ms, tokens
+
+    res = {}
+    for name, r, split, lora in (("rank32", 32, False, "gated"), ("base_fused", 32, False, "off"),
+                                 ("rank128", 128, True, "gated"), ("base_split", 128, True, "off")):
+        lw = layers(r, split)
+        ms, tokens = run(lw, lora)
+        del lw
+        res[name] = (ms, tokens)
+        log(f"[bench] forward {name}: {ms:.3f} ms per step, {tokens} tokens in {steps} steps")
+    out = {
+        "workload": (f"whole forward of the step: {L} layers (RMSNorm, gated Q|K|V, attention, gated O, RMSNorm, "
+                     f"SwiGLU MLP {H}->{2 * I}->{H}), final norm, LM head {H}->{V} with chunk statistics, accept, "
+                     "KV commit, block assembly; random weights"),
+        "ms_per_step": {k: round(v[0], 3) for k, v in res.items()},
+        "tokens_per_s": {k: round(v[1] / (v[0] * steps / 1e3), 1) for k, v in res.items()},
+        "alpha": {"rank32": round(res["rank32"][0] / res["base_fused"][0], 4),
+                  "rank128": round(res["rank128"][0] / res["base_split"][0], 4)},
+        "alpha_pages": 1.12,
+        "steps": steps,
+        "note": ("random weights give flat, unrelated p and q rows, so few drafts pass: the tokens per step here "
+                 "are not the calibrated workload's; alpha is a ratio of step times on the same trajectory shape"),
+    }
+    return out
+
+
 def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=None):
     """The oracle, as it stands, on a bounded sample of the same workload
     (about 10 s on 16 host cores): (a) block attention + gated Q/K/V/O
@@ -400,6 +519,10 @@ def main():
                          "isd_kv_write of the whole block before each attention call")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip the LM-head leg (isd_lm_head timed after the steps; not part of the step)")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip the whole-forward leg (every layer with its MLP, LM head, accept on its statistics; "
+                         "rank 32 and 128 against the base projections)")
+    ap.add_argument("--forward-steps", type=int, default=6, help="timed steps of each whole-forward configuration")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -716,6 +839,10 @@ def main():
         del logits[:]
         torch.cuda.empty_cache()
         res["lm_head"] = lm_head_leg(cfg, dev)
+    if not args.no_forward and args.workload == "8b":
+        del logits[:]
+        torch.cuda.empty_cache()
+        res["forward"] = forward_leg(cfg, st, dev, args.slices, steps=args.forward_steps)
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
         res["cpu_baseline"] = (cpu_baseline(cfg) if args.workload == "8b" else

@@ -19,11 +19,18 @@ from . import (KVCache, accept_workspace, isd_attention_workspace_size, isd_lm_h
 
 
 class LayerWeights:
-    """bf16 weights of one decoder layer (Q|K|V fused, gate|up fused)."""
+    """bf16 weights of one decoder layer (Q|K|V fused, gate|up fused).
 
-    def __init__(self, g1, g2, Wqkv, Wo, Wgu, Wd, Aqkv=None, Bqkv=None, Ao=None, Bo=None):
+    The gated LoRA of Q, K and V is either one stacked adapter on the fused
+    projection (Aqkv [3r, H], Bqkv block-diagonal [(Hq+2Hkv)D, 3r]) or, when
+    `qkv_adapters` is given as three (A, B) pairs, one adapter per
+    projection; Q, K and V then run as three projections (the adapter's rank
+    is at most 128 per call)."""
+
+    def __init__(self, g1, g2, Wqkv, Wo, Wgu, Wd, Aqkv=None, Bqkv=None, Ao=None, Bo=None, qkv_adapters=None):
         self.g1, self.g2, self.Wqkv, self.Wo, self.Wgu, self.Wd = g1, g2, Wqkv, Wo, Wgu, Wd
         self.Aqkv, self.Bqkv, self.Ao, self.Bo = Aqkv, Bqkv, Ao, Bo
+        self.qkv_adapters = qkv_adapters
 
 
 class Forward:
@@ -55,10 +62,20 @@ class Forward:
         self.yqkv, self.q, self.att = e(M, nq), e(C, R, Hq, D, dt=bf), e(C, R, Hq, D)
         self.ob, self.yo = e(M, Hq * D, dt=bf), e(M, H)
         self.gu, self.act, self.yd = e(M, 2 * I), e(M, I, dt=bf), e(M, H)
-        self.logits = e(C, R, V, dt=bf)
+        # two logits buffers, alternated step by step: the accept step reads
+        # the previous step's block for its residual draws
+        self.logits_buf = [e(C, R, V, dt=bf), e(C, R, V, dt=bf)]
+        self.logits = self.logits_buf[0]
         self.nch = (V + 8191) // 8192
         self.stats = e(C, R, self.nch, 2)
-        r_max = max([0] + [w.Aqkv.shape[0] for w in layers if w.Aqkv is not None])
+        ranks = [w.Ao.shape[0] for w in layers if w.Ao is not None]
+        ranks += [w.Aqkv.shape[0] for w in layers if w.Aqkv is not None]
+        ranks += [a.shape[0] for w in layers if w.qkv_adapters for a, _ in w.qkv_adapters]
+        r_max = max([0] + ranks)
+        split = layers[0].qkv_adapters is not None
+        widths = [Hq * D, Hkv * D, Hkv * D]
+        if split:  # one fp32 output per projection
+            self.yparts = [e(M, wd) for wd in widths]
         self.lora_ws = e(max(isd_lora_workspace_size(M, max(r_max, 16)), 256) // 4)
         need = isd_attention_workspace_size(kvs[0], C, R, Hq, max_len, slices)
         self.att_ws = e(max(need, 256) // 4 + 1)
@@ -68,11 +85,24 @@ class Forward:
         for l, w in enumerate(layers):
             c = self.calls
             c.append(prepare_rmsnorm(self.h, w.g1, self.x, delta=prev_delta))
-            if lora == "gated":
-                c.append(prepare_linear_gated(self.x, w.Wqkv, w.Aqkv, w.Bqkv, mask, self.yqkv, self.lora_ws))
+            if split:
+                r0 = 0
+                for j, wd in enumerate(widths):
+                    Wj = w.Wqkv[r0:r0 + wd]
+                    if lora == "gated":
+                        A, B = w.qkv_adapters[j]
+                        c.append(prepare_linear_gated(self.x, Wj, A, B, mask, self.yparts[j], self.lora_ws))
+                    else:
+                        c.append(prepare_linear(self.x, Wj, self.yparts[j]))
+                    r0 += wd
+                for y, dst in zip(self.yparts, (self.q, k_all[l], v_all[l])):
+                    c.append(prepare_cast_bf16(y, [dst]))
             else:
-                c.append(prepare_linear(self.x, w.Wqkv, self.yqkv))
-            c.append(prepare_cast_bf16(self.yqkv, [self.q, k_all[l], v_all[l]]))
+                if lora == "gated":
+                    c.append(prepare_linear_gated(self.x, w.Wqkv, w.Aqkv, w.Bqkv, mask, self.yqkv, self.lora_ws))
+                else:
+                    c.append(prepare_linear(self.x, w.Wqkv, self.yqkv))
+                c.append(prepare_cast_bf16(self.yqkv, [self.q, k_all[l], v_all[l]]))
             c.append(prepare_attention(kvs[l], self.q, ctx, max_len, self.att, ws=self.att_ws, slices=slices,
                                        dev_err=dev_err, k_blk=k_all[l], v_blk=v_all[l]))
             c.append(prepare_cast_bf16(self.att.view(M, Hq * D), [self.ob]))
@@ -86,14 +116,15 @@ class Forward:
             c.append(prepare_linear(self.act, w.Wd, self.yd))
             prev_delta = self.yd
         self.calls.append(prepare_rmsnorm(self.h, gf, self.xf, delta=prev_delta))
-        self.calls.append(prepare_lm_head(self.xf, Wlm, self.logits.view(M, V), self.stats.view(M, self.nch, 2),
-                                          self.lm_ws))
-        self.lm_head_call = self.calls[-1]
+        self.lm_head_calls = [prepare_lm_head(self.xf, Wlm, lg.view(M, V), self.stats.view(M, self.nch, 2),
+                                              self.lm_ws) for lg in self.logits_buf]
 
-    def __call__(self, h0):
+    def __call__(self, h0, parity=0):
         """Runs the forward from the residual stream h0 [C*R, H] (fp32, the
-        block's embeddings); leaves logits and chunk statistics in
-        self.logits / self.stats."""
+        block's embeddings); leaves the logits in self.logits_buf[parity]
+        (also self.logits) and their chunk statistics in self.stats."""
         self.h.copy_(h0)
         for f in self.calls:
             f()
+        self.lm_head_calls[parity]()
+        self.logits = self.logits_buf[parity]
