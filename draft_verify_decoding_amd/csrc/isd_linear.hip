@@ -564,10 +564,10 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
 template <int R16>
 hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   const long cus = isd_device_cus_internal();
-  constexpr int kShapes[4][2] = {{1, 3}, {2, 2}, {1, 2}, {1, 1}};
-  int pick = 3;
+  constexpr int kShapes[5][2] = {{2, 3}, {1, 3}, {2, 2}, {1, 2}, {1, 1}};
+  int pick = 4;
   long best = -1;
-  for (int i = p.splits == 1 ? 0 : 3; i < 4; ++i) {
+  for (int i = p.splits == 1 ? 0 : 4; i < 5; ++i) {
     const int tm = kShapes[i][0], tn = kShapes[i][1];
     const long wgs = static_cast<long>((p.M + 64 * tm - 1) / (64 * tm)) * ((p.Nout + 64 * tn - 1) / (64 * tn)) * p.splits;
     const long cost = (wgs + cus - 1) / cus * (64 * tm + 64 * tn);
@@ -579,9 +579,10 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
     if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
   switch (pick) {
-    case 0: return launch_tile<1, 3, 4, R16>(p, stream);
-    case 1: return launch_tile<2, 2, 4, R16>(p, stream);
-    case 2: return launch_tile<1, 2, 4, R16>(p, stream);
+    case 0: return launch_tile<2, 3, 3, R16>(p, stream);
+    case 1: return launch_tile<1, 3, 4, R16>(p, stream);
+    case 2: return launch_tile<2, 2, 4, R16>(p, stream);
+    case 3: return launch_tile<1, 2, 4, R16>(p, stream);
     default: return launch_tile<1, 1, 5, R16>(p, stream);
   }
 }

@@ -160,3 +160,29 @@ def test_large_batch_uses_the_wide_tile_with_same_bits():
     want = ref.gated_lora(x[rows].double().numpy(), W.double().numpy(), A.double().numpy(),
                           B.double().numpy(), mask[rows], 2.0)
     assert rel_err(fused.cpu()[rows].double().numpy(), want) < 2e-3
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_wide_projection_tile_same_bits(gated):
+    """The MLP's fused gate|up width (512 rows, 24,576 outputs) picks the
+    128x192 tile; sampled rows match the oracle, clean rows equal the base
+    projection, and rows equal bit for bit the same rows computed in a small
+    launch (another tile)."""
+    x, W, A, B, mask = case(8, 512, 1024, 24576, 32)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    base = dvd.isd_linear(xd, Wd)
+    if gated:
+        y = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=1.0)
+        small = dvd.isd_linear_gated(xd[100:140].contiguous(), Wd, Ad, Bd, md[100:140].contiguous(), scale=1.0)
+    else:
+        y = base
+        small = dvd.isd_linear(xd[100:140].contiguous(), Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(y[100:140].view(torch.int32), small.view(torch.int32))
+    m = torch.from_numpy(mask).to(DEV)
+    assert torch.equal(y[~m].view(torch.int32), base[~m].view(torch.int32))
+    rows = np.array([0, 5, 127, 128, 300, 511])
+    want = ref.gated_lora(x[rows].double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(),
+                          mask[rows], 1.0 if gated else 0.0)
+    assert rel_err(y.cpu()[rows].double().numpy(), want) < 2e-3
