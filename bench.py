@@ -46,6 +46,7 @@ PROBE_EVERY = 8  # timed steps between the ones bracketed with HIP events
 CFG = dict(C=64, N=4, Hq=32, Hkv=8, D=128, layers=36, V=151936, hidden=4096, intermediate=12288, lora_rank=32,
            ctx=("uniform", 1024, 8192), accept=0.9, sigma_l=3.0, seed=3, proposal="sample")
 CFG_32B = dict(CFG, C=16, Hq=64, Hkv=8, D=128, layers=64, hidden=5120, intermediate=25600, ctx=16384)
+CFG_8B1 = dict(CFG, C=1, ctx=4096)  # the single-sequence 8B step
 
 
 def log(*a):
@@ -505,11 +506,11 @@ def main():
                     help="projections with the gated LoRA of R-ISD (default) or the base GEMM alone "
                          "(the ratio of the two step times is the LoRA overhead alpha)")
     ap.add_argument("--graph", action="store_true",
-                    help="replay each step as a captured HIP graph (two graphs: even and odd steps); every "
-                         f"{PROBE_EVERY}th timed step runs eagerly with the event probes")
-    ap.add_argument("--workload", choices=("8b", "32b"), default="8b",
-                    help="8b: C=64 ragged 1k-8k contexts, 36 layers (default); 32b: C=16 contexts of 16,384, "
-                         "64 layers of 64/8 heads, hidden 5120")
+                    help="replay each step as a captured HIP graph (one per step, holding that step's logits "
+                         f"rows); every {PROBE_EVERY}th timed step runs eagerly with the event probes")
+    ap.add_argument("--workload", choices=("8b", "8b1", "32b"), default="8b",
+                    help="8b: C=64 ragged 1k-8k contexts, 36 layers (default); 8b1: one sequence of 4,096 cached "
+                         "tokens, 36 layers; 32b: C=16 contexts of 16,384, 64 layers of 64/8 heads, hidden 5120")
     ap.add_argument("--N", type=int, default=4, help="stride N (2N-row blocks); default 4")
     ap.add_argument("--accept", type=float, default=0.9, choices=(0.5, 0.7, 0.9),
                     help="mean per-draft acceptance the draft noise is set for; default 0.9")
@@ -533,7 +534,7 @@ def main():
         # at 16,384-token contexts, 66 tiles give 8 chunks per sequence and
         # 16 x 8 x 2 head groups = 256 workgroups, one round on 256 CUs
         # (64 tiles would give a ninth, one-tile chunk and 288 workgroups).
-        args.slices = -64 if args.workload == "8b" else -66
+        args.slices = {"8b": -64, "8b1": -4, "32b": -66}[args.workload]
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return
@@ -555,8 +556,8 @@ def main():
 
     import draft_verify_decoding_amd as dvd
 
-    cfg = dict(CFG if args.workload == "8b" else CFG_32B, proposal=args.proposal, lora=args.lora, N=args.N,
-               accept=args.accept)
+    cfg = dict({"8b": CFG, "8b1": CFG_8B1, "32b": CFG_32B}[args.workload], proposal=args.proposal, lora=args.lora,
+               N=args.N, accept=args.accept)
     commit_mode = args.kv == "commit"
     default_workload = args.workload == "8b" and args.N == 4
     dev = "cuda"
@@ -615,16 +616,12 @@ def main():
     acc_ev = [(ev(), ev()) for _ in probes]
     com_ev = [ev() for _ in probes]  # end of the KV commit (after the accept's end event)
 
-    # --graph: the whole step on one side stream, the logits of step t copied
-    # by the device (index from a step word in HBM) into one of two fixed
-    # buffers, the accept reading its Philox step from that word; captured
-    # once per parity and replayed.
+    # --graph: the whole step on one side stream, captured once per step: each
+    # step's graph holds that step's logits and the previous step's (the
+    # pre-generated teacher rows stay where they are, so no copy runs), the
+    # state buffers of its parity and its step number. Replayed in order.
     gs = torch.cuda.Stream() if args.graph else None
     if args.graph:
-        all_lg = torch.stack(logits)
-        del logits[:]
-        buf = [torch.empty_like(all_lg[0]) for _ in range(2)]
-        step_t = torch.zeros(1, dtype=torch.int64, device=dev)
         with torch.cuda.stream(gs):
             layer_calls = []
             for l in range(L):
@@ -646,13 +643,15 @@ def main():
 
     def step(t, timed_idx=None):
         if args.graph:
-            par = t % 2
             with torch.cuda.stream(gs):
                 if timed_idx is None:
-                    graphs[par].replay()
+                    graphs[t].replay()
                 else:
-                    graph_body(par, timed_idx)
+                    body(t, timed_idx)
             return
+        body(t, timed_idx)
+
+    def body(t, timed_idx=None):
         for l in range(L):
             c = layer_calls[l]
             if timed_idx is not None:
@@ -677,58 +676,25 @@ def main():
         if timed_idx is not None:
             acc_ev[timed_idx][0].record()
         dvd.isd_accept(logits[t], logits[t - 1] if t else None, s_in, s_out, N, cfg["seed"], t, out=acc_out,
-                       ws=acc_ws, ctx=ctx, dev_err=err, proposal=cfg["proposal"])
+                       ws=acc_ws, ctx=ctx, dev_err=err, proposal=cfg["proposal"], stream=gs)
         if timed_idx is not None:
             acc_ev[timed_idx][1].record()
         if commit is not None:
             commit()
             if timed_idx is not None:
                 com_ev[timed_idx].record()
-
-    def graph_body(par, timed_idx=None):
-        torch.index_select(all_lg, 0, step_t, out=buf[par].unsqueeze(0))
-        for l in range(L):
-            c = layer_calls[l]
-            if timed_idx is not None:
-                proj_ev[timed_idx][l][0].record()
-            for f in c["qkv"]:
-                f()
-            if timed_idx is not None:
-                proj_ev[timed_idx][l][1].record()
-            if c["kvw"] is not None:
-                c["kvw"]()
-            if timed_idx is not None:
-                att_ev[timed_idx][l][0].record()
-            c["att"]()
-            if timed_idx is not None:
-                att_ev[timed_idx][l][1].record()
-            c["o"]()
-            if timed_idx is not None:
-                proj_ev[timed_idx][l][2].record()
-        s_in, s_out = (s_a, s_b) if par == 0 else (s_b, s_a)
-        if commit is not None:
-            ctx_prev.copy_(ctx)
-        if timed_idx is not None:
-            acc_ev[timed_idx][0].record()
-        dvd.isd_accept(buf[par], buf[1 - par], s_in, s_out, N, cfg["seed"], 0, out=acc_out, ws=acc_ws, ctx=ctx,
-                       dev_err=err, proposal=cfg["proposal"], step_dev=step_t, stream=gs)
-        if timed_idx is not None:
-            acc_ev[timed_idx][1].record()
-        if commit is not None:
-            commit()
-            if timed_idx is not None:
-                com_ev[timed_idx].record()
-        step_t.add_(1)
 
     if args.graph:
-        graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+        graphs = {}
         torch.cuda.synchronize()
-        for par in (0, 1):
-            with torch.cuda.graph(graphs[par], stream=gs):
-                graph_body(par)
+        t_cap = time.perf_counter()
+        for t in range(total):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                body(t)
+            graphs[t] = g
         torch.cuda.synchronize()
-        assert int(step_t.item()) == 0  # capture records, it does not run
-        log("[bench] step captured as two HIP graphs")
+        log(f"[bench] {total} steps captured as HIP graphs in {time.perf_counter() - t_cap:.1f} s")
 
     for t in range(W):
         step(t)
@@ -765,8 +731,11 @@ def main():
     att_only_tps = probe_tokens / ((np.sum(att_ms) + np.sum(acc_ms)) / 1e3)
 
     res = {
-        "metric": (METRIC if args.workload == "8b" else
-                   f"ISD accepted tokens/s at C={C},N={N} (32B shapes); attn+accept HBM GB/s vs peak"),
+        "metric": {"8b": METRIC,
+                   "8b1": f"ISD accepted tokens/s at C=1,N={N} (8B shapes, context 4096); attn+accept HBM GB/s "
+                          "vs peak",
+                   "32b": f"ISD accepted tokens/s at C={C},N={N} (32B shapes); attn+accept HBM GB/s vs peak"}[
+                       args.workload],
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -780,11 +749,12 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"stationary batch C={C}, N={N} ({R}-row blocks), "
-                         + ("8B-class GQA 32/8 heads, head_dim 128, 36 layers, hidden 4096, "
-                            if args.workload == "8b" else
-                            "32B-class GQA 64/8 heads, head_dim 128, 64 layers, hidden 5120, ")
+                         + ("32B-class GQA 64/8 heads, head_dim 128, 64 layers, hidden 5120, "
+                            if args.workload == "32b" else
+                            "8B-class GQA 32/8 heads, head_dim 128, 36 layers, hidden 4096, ")
                          + "bf16 paged KV (16-token pages), "
-                         + ("contexts U{1024..8192}" if args.workload == "8b" else "contexts 16384")
+                         + {"8b": "contexts U{1024..8192}", "8b1": "context 4096",
+                            "32b": "contexts 16384"}[args.workload]
                          + f", vocab 151936, acceptance ~{cfg['accept']}, "
                          + ("gated-LoRA rank-32" if args.lora == "gated" else "base (no LoRA)")
                          + " Q/K/V/O projections; MLP and LM head not included"),
@@ -839,14 +809,16 @@ def main():
         del logits[:]
         torch.cuda.empty_cache()
         res["lm_head"] = lm_head_leg(cfg, dev)
-    if not args.no_forward and args.workload == "8b":
+    if not args.no_forward and args.workload in ("8b", "8b1"):
         del logits[:]
         torch.cuda.empty_cache()
         res["forward"] = forward_leg(cfg, st, dev, args.slices, steps=args.forward_steps)
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
-        res["cpu_baseline"] = (cpu_baseline(cfg) if args.workload == "8b" else
-                               cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14, layers_timed=8))
+        res["cpu_baseline"] = {"8b": lambda: cpu_baseline(cfg),
+                               "8b1": lambda: cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14),
+                               "32b": lambda: cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14,
+                                                           layers_timed=8)}[args.workload]()
         log(f"[bench] cpu baseline took {time.perf_counter() - t_cpu:.1f} s")
     print(json.dumps(res), flush=True)
 

@@ -18,19 +18,33 @@ FLAGS = [
 
 
 def build(verbose=False):
+    """Compile every source to an object (in parallel, one hipcc each), then
+    link them into libisd.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    incs = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(dir=HERE, prefix="_build") as obj_dir:
+        def run(cmd):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+            if res.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + err)
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+
+        objs = [os.path.join(obj_dir, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[hipcc, *compile_flags, *incs, "-c", os.path.join(HERE, "csrc", s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            list(ex.map(run, cmds))
+        run([hipcc, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -718,15 +718,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // Log-sum-exp merge of the pieces of one (sequence, KV head, query block)
 // held by several slices, in slice order (an online rescale, so the pieces
-// are read once). Thread t owns query column t/8 and D/8 consecutive dims,
-// read and written as float4; the (max, sum) and vectors of up to eight
-// pieces are loaded together before any is combined.
+// are read once). A workgroup takes 32 dims of the block's 32 query
+// columns: thread t owns column t/8 and one float4 of dims; the (max, sum)
+// and vectors of up to sixteen pieces are loaded together before any is
+// combined. Every thread of a column runs the same (max, sum) recurrence,
+// so how the dims are spread over threads does not change any value.
 template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   const int MB = p.MB;
   const int b = blockIdx.x / p.Hkv;
   const int g = blockIdx.x % p.Hkv;
-  const int qb = blockIdx.y;
+  const int qb = blockIdx.y / (D / 32);
   const int G = p.G;
   const int hg = g / p.HPW, hl_w = g % p.HPW;
   // Pieces j = 0 .. n-1 of the sequence, in order: its slices wa .. wb
@@ -749,11 +751,11 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
     n = slice_of(tb1 - 1) - wa + 1;
   }
   if (n == 1) return;  // finalised by the main launch
-  constexpr int kDimsPerThread = D * 32 / 256;
+  constexpr int kDimsPerThread = 4;
   constexpr int kV = kDimsPerThread / 4;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const int col = qb * 32 + threadIdx.x / (256 / 32);
-  const int d0 = (threadIdx.x % (256 / 32)) * kDimsPerThread;
+  const int d0 = (blockIdx.y % (D / 32)) * 32 + (threadIdx.x % (256 / 32)) * kDimsPerThread;
   if (col >= p.M) return;
   auto piece = [&](int j) {
     size_t pidx;
@@ -772,8 +774,8 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   f32x4 acc[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // batches of B pieces, B the smallest of 2, 4, 8 that holds n (the same
-  // arithmetic for every B: one online step per piece, in order)
+  // batches of B pieces, B the smallest of 2, 4, 8, 16 that holds n (the
+  // same arithmetic for every B: one online step per piece, in order)
   auto merge_all = [&](auto batch) {
     constexpr int B = decltype(batch)::value;
     for (int j0 = 0; j0 < n; j0 += B) {
@@ -806,6 +808,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   };
   if (n <= 2) merge_all(std::integral_constant<int, 2>{});
   else if (n <= 4) merge_all(std::integral_constant<int, 4>{});
+  else if (n <= 8) merge_all(std::integral_constant<int, 8>{});
   else merge_all(std::integral_constant<int, kBatch>{});
   const int hl = col / p.rows, i = col % p.rows;
   const int h = g * p.group + hl;
@@ -991,8 +994,9 @@ hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t s
     if (share) hipLaunchKernelGGL((attention_kernel<E, D, false, std::is_same<E, uint16_t>::value>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((attention_kernel<E, D, false, false>), grid, block, 0, stream, p);
   }
-  hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(p.MB)),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attention_merge_kernel<D>),
+                     dim3(static_cast<unsigned>(p.C * p.Hkv), static_cast<unsigned>(p.MB * (D / 32))), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -1114,17 +1118,28 @@ int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk,
   p.HPW = plan.HPW;
   p.CT = plan.CT;
   p.Kmax = plan.Kmax;
+  int groups = plan.groups;
+  if (plan.CT > 0) {
+    // Few sequences and chunks (a single sequence, say) give fewer
+    // workgroups than CUs. The heads per workgroup only group waves into
+    // workgroups: a wave's arithmetic and the place of its partial in the
+    // workspace do not depend on them. So they are halved until the grid
+    // covers the CUs (the bound takes every sequence at max_len).
+    const long cus = isd_device_cus_internal();
+    while (p.HPW > 1 && static_cast<long>(p.Hkv / p.HPW) * p.G < cus) p.HPW /= 2;
+    groups = p.Hkv / p.HPW;
+  }
   p.scale_log2 = scale * kLog2e;
   p.k_blk = k_blk;
   p.v_blk = v_blk;
 
   hipError_t e;
   if (kv->dtype == ISD_BF16)
-    e = kv->head_dim == 128 ? launch_attention_typed<uint16_t, 128>(p, plan.groups, stream)
-                            : launch_attention_typed<uint16_t, 64>(p, plan.groups, stream);
+    e = kv->head_dim == 128 ? launch_attention_typed<uint16_t, 128>(p, groups, stream)
+                            : launch_attention_typed<uint16_t, 64>(p, groups, stream);
   else
-    e = kv->head_dim == 128 ? launch_attention_typed<float, 128>(p, plan.groups, stream)
-                            : launch_attention_typed<float, 64>(p, plan.groups, stream);
+    e = kv->head_dim == 128 ? launch_attention_typed<float, 128>(p, groups, stream)
+                            : launch_attention_typed<float, 64>(p, groups, stream);
   return e == hipSuccess ? ISD_OK : ISD_E_LAUNCH;
 }
 

@@ -483,6 +483,159 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   }
 }
 
+// Few rows (M <= 32: one sequence's stride block, or a handful): the tiled
+// kernel would give Nout / 64 .. Nout / 192 workgroups, far fewer than CUs,
+// each streaming its W columns with a few slabs in flight. Here one wave,
+// as a workgroup of its own, owns one 32-column block of the output over
+// the whole of K (Nout / 32 workgroups) and keeps S slabs in flight, as
+// many as the wave's vector-memory counter tracks. A slab is the x rows
+// (AL direct loads of 8 rows) and the block's 32 W rows (four loads), in
+// the tiled kernel's swizzled LDS layout. Each 32x32 output block runs the
+// tiled kernel's MFMA sequence, the same instruction on the same operands
+// slab by slab in ascending K, and the gated epilogue is the tiled
+// kernel's: every output has the bits the tiled kernel gives it.
+template <int AL>
+struct SkinnyShape {
+  static constexpr int kLoads = AL + 4;  // 1 KB direct loads per slab
+  static constexpr int S = 1 + 63 / kLoads < 12 ? 1 + 63 / kLoads : 12;  // slabs in flight + the one multiplied
+  static constexpr int kARows = 8 * AL;
+  static constexpr int STAGE = (kARows + 32) * kBK;  // elements
+};
+
+template <int AL, int R16>
+__global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
+  using SK = SkinnyShape<AL>;
+  constexpr int S = SK::S, STAGE = SK::STAGE, kARows = SK::kARows, kLoads = SK::kLoads;
+  static_assert(S >= 3 && S <= 12, "stage count");
+  static_assert((S - 2) * kLoads < 64, "loads in flight fit the counter");
+  // one LDS object per stage, as in the tiled kernel
+#define ISD_SK_STAGE(i) __shared__ __attribute__((aligned(16))) uint16_t sk##i[S > i ? STAGE : 8];
+  ISD_SK_STAGE(0) ISD_SK_STAGE(1) ISD_SK_STAGE(2) ISD_SK_STAGE(3) ISD_SK_STAGE(4) ISD_SK_STAGE(5)
+  ISD_SK_STAGE(6) ISD_SK_STAGE(7) ISD_SK_STAGE(8) ISD_SK_STAGE(9) ISD_SK_STAGE(10) ISD_SK_STAGE(11)
+#undef ISD_SK_STAGE
+  auto stage_ptr = [&](int stage) -> uint16_t* {
+    switch (stage) {
+#define ISD_CASE(i) \
+  case i:           \
+    if constexpr (S > i) return sk##i;
+      ISD_CASE(1) ISD_CASE(2) ISD_CASE(3) ISD_CASE(4) ISD_CASE(5) ISD_CASE(6) ISD_CASE(7) ISD_CASE(8) ISD_CASE(9)
+      ISD_CASE(10) ISD_CASE(11)
+#undef ISD_CASE
+      default: return sk0;
+    }
+  };
+  constexpr int kR16 = R16 > 0 ? R16 : 1;
+  constexpr int kUStride = 16 * R16 + 4;  // U rows in LDS, padded as in the tiled kernel
+  __shared__ __attribute__((aligned(16))) float s_u[R16 > 0 ? kARows * kUStride : 4];
+
+  const int lane = threadIdx.x, lane32 = lane & 31, hh = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  // Load q of a slab fills 8 LDS rows, lane i row i / 8 at slot i % 8,
+  // with the chunk the swizzle puts there (chunk c of row r sits at slot
+  // c ^ (r % 8) ^ ((r / 8) % 2)). x rows past M read row M - 1 and W rows
+  // past Nout row Nout - 1: such rows and columns are never stored.
+  const int g_row = lane >> 3;
+  const uint16_t* a_src[AL];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int q = 0; q < AL; ++q)
+    a_src[q] = p.x + static_cast<long>(min(8 * q + g_row, p.M - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    b_src[q] = p.w + static_cast<long>(min(n0 + 8 * q + g_row, p.Nout - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
+  auto load_slab = [&](int k0, int stage) {
+    uint16_t* base = stage_ptr(stage);
+#pragma unroll
+    for (int q = 0; q < AL; ++q) load_lds16(a_src[q] + k0, base + 8 * q * kBK);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_lds16(b_src[q] + k0, base + (kARows + 8 * q) * kBK);
+  };
+
+  // Operand rows of this lane: W row lane32 of the block, x row lane32
+  // (lanes past the staged x rows read a staged row; their output rows are
+  // at or past M).
+  const int ra = lane32 & (kARows - 1);
+  const int swa = (ra & 7) ^ ((ra >> 3) & 1), swb = (lane32 & 7) ^ ((lane32 >> 3) & 1);
+  f32x16 acc = {};
+  auto compute = [&](int stage) {
+    const uint16_t* sA = stage_ptr(stage);
+    const uint16_t* sB = sA + kARows * kBK;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sA[ra * kBK + ((2 * s + hh) ^ swa) * 8]));
+      b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sB[lane32 * kBK + ((2 * s + hh) ^ swb) * 8]));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+  };
+
+  const int nk = p.K / kBK;
+#pragma unroll
+  for (int d = 0; d < S - 1; ++d) load_slab(min(d, nk - 1) * kBK, d);
+
+  // Gated: while the first slabs are in flight, the U rows (split-K
+  // partials summed in split order, as the tiled kernel sums them) go to
+  // LDS and the B fragments and mask bits to registers.
+  int mine = 0;
+  BFrag<kR16> bfr;
+  if constexpr (R16 > 0) {
+    constexpr int r4 = 4 * R16;
+    const long pstride = static_cast<long>(p.M) * 16 * R16;
+    for (int e = lane; e < p.M * r4; e += 64) {
+      const int row = e / r4, q = e % r4;
+      const float* src = p.u + static_cast<long>(row) * 16 * R16 + 4 * q;
+      f32x4 part[kMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        part[sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
+      f32x4 v = part[0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplits; ++sp)
+        if (sp < p.u_splits)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
+      *reinterpret_cast<f32x4*>(&s_u[row * kUStride + 4 * q]) = v;
+    }
+    bfr = b_frag<R16>(p.b, p.Nout, n0, lane32, hh);
+    mine = lane32 < p.M ? p.mask[lane32] != 0 : 0;
+  }
+
+  // unrolled over S slabs, so every stage index is a constant (as in the
+  // tiled kernel); one wave, so the waits alone order the stages
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+    for (int d = 0; d < S; ++d) {
+      const int kt = kt0 + d;
+      if (kt >= nk) break;
+      // slab kt has landed once only the S-2 later slabs' loads may be in
+      // flight, and the reads of slab kt-1's stage (the one the next load
+      // overwrites) are done once no LDS operation is
+      wait_vm_lgkm0<(S - 2) * kLoads>();
+      load_slab(min(kt + S - 1, nk - 1) * kBK, (d + S - 1) % S);
+      compute(d);
+    }
+  }
+  wait_vm_lgkm0<0>();
+
+  // Epilogue (the tiled kernel's): register e of lane (j, hh) is row
+  // 8(e/4) + 4hh + e%4, column j; a MASK row takes acc + scale * delta.
+  int live = 0;
+  f32x16 dl = {};
+  if constexpr (R16 > 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) live |= __shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) << e;
+    if (__any(live)) dl = lora_delta<R16>(u_frag<R16>(lane32 < p.M ? &s_u[lane32 * kUStride] : nullptr, hh), bfr);
+  }
+  const int col = n0 + lane32;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
+    if (row < p.M && col < p.Nout)
+      p.y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e];
+  }
+}
+
 // y[m] += scale * (U B^T)[m] on MASK rows only, one wave per 32x32 tile of
 // y; tiles without a MASK row are skipped and clean rows are never written.
 // The delta is the GEMM epilogue's, instruction for instruction.
@@ -578,6 +731,13 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   }
   if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
     if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
+  if (p.splits == 1 && p.M <= 32) {  // few rows: one wave per 32 output columns
+    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32));
+    if (p.M <= 8) hipLaunchKernelGGL((gemm_skinny_kernel<1, R16>), grid, dim3(64), 0, stream, p);
+    else if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<2, R16>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<4, R16>), grid, dim3(64), 0, stream, p);
+    return hipGetLastError();
+  }
   switch (pick) {
     case 0: return launch_tile<2, 3, 3, R16>(p, stream);
     case 1: return launch_tile<1, 3, 4, R16>(p, stream);

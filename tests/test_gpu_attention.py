@@ -157,11 +157,43 @@ def test_bad_page_id_sets_device_flag():
     assert err.item() & dvd.DEV_PAGE_OOB
 
 
-def test_8b_single_sequence_context_4096():
-    """C=1, N=4, 32/8 heads, D=128, 4096 cached tokens: every output checked."""
+@pytest.mark.parametrize("slices", [0, dvd.attn_invariant(4), dvd.attn_invariant(1)])
+def test_8b_single_sequence_context_4096(slices):
+    """C=1, N=4, 32/8 heads, D=128, 4096 cached tokens: every output checked,
+    in the stream-K split and in the batch-invariant split with chunks of 4
+    tiles (the single-sequence step's launch) and of 1 tile."""
     case = workload.AttentionCase(2, C=1, rows=8, Hq=32, Hkv=8, D=128, ctx=4096)
-    got, want = run(case)
+    got, want = run(case, slices=slices)
     assert slab_errors(got, want).max() < 2e-3
+
+
+@pytest.mark.parametrize("t", [4, 1])
+def test_single_sequence_equals_its_rows_in_a_wide_batch(t):
+    """A single sequence runs on a grid of its own shape (few chunks: one KV
+    head per workgroup) and a 64-sequence batch on another (eight heads per
+    workgroup); the sequence's rows come out bit for bit the same in both,
+    with the batch-invariant split."""
+    C, rows = 64, 8
+    ctx = np.full(C, 1024, np.int64)
+    ctx[17] = 4096
+    case = workload.AttentionCase(12, C=C, rows=rows, Hq=32, Hkv=8, D=128, ctx=ctx)
+    print(f"single sequence in a batch t={t}", flush=True)
+    kv, err = fill_cache(case)
+    max_len = int(case.lengths.max())
+    ctx_d = torch.from_numpy(case.ctx.astype(np.int32)).to(DEV)
+    q = case.q.to(DEV)
+    inv = dvd.attn_invariant(t)
+    batch = dvd.isd_attention(kv, q, ctx_d, max_len=max_len, slices=inv, dev_err=err)
+    solo_kv = copy.copy(kv)
+    solo_kv.block_table = kv.block_table[17:18].contiguous()
+    solo = dvd.isd_attention(solo_kv, q[17:18].contiguous(), ctx_d[17:18].contiguous(), max_len=max_len,
+                             slices=inv, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(bits(solo), bits(batch[17:18]))
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q)[17:18], kp, vp, case.table[17:18], case.ctx[17:18])
+    assert slab_errors(solo.cpu().double().numpy(), want).max() < 2e-3
 
 
 @pytest.mark.parametrize("N", [2, 3, 4, 6, 8])

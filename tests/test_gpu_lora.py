@@ -186,3 +186,44 @@ def test_wide_projection_tile_same_bits(gated):
     want = ref.gated_lora(x[rows].double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(),
                           mask[rows], 1.0 if gated else 0.0)
     assert rel_err(y.cpu()[rows].double().numpy(), want) < 2e-3
+
+
+@pytest.mark.parametrize("M", [1, 8, 13, 32])
+@pytest.mark.parametrize("r", [0, 32, 96, 128])
+def test_few_rows_same_bits_as_the_tiled_kernel(M, r):
+    """Up to 32 rows (a single sequence's stride block and a few more) run
+    one wave per 32 output columns over the whole of K; their outputs equal,
+    bit for bit, the same rows inside a 512-row launch (the tiled kernel),
+    base and gated, and match the oracle. The fused Q|K|V width, 6144."""
+    K, Nout = 4096, 6144
+    x, W, A, B, mask = case(9, 512, K, Nout, max(r, 16))
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    if r:
+        full = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=1.0)
+        few = dvd.isd_linear_gated(xd[:M].contiguous(), Wd, Ad, Bd, md[:M].contiguous(), scale=1.0)
+    else:
+        full = dvd.isd_linear(xd, Wd)
+        few = dvd.isd_linear(xd[:M].contiguous(), Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(few.view(torch.int32), full[:M].view(torch.int32))
+    want = ref.gated_lora(x[:M].double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(),
+                          mask[:M], 1.0 if r else 0.0)
+    assert rel_err(few.cpu().double().numpy(), want) < 2e-3
+
+
+@pytest.mark.parametrize("M,K,Nout", [(8, 64, 200), (5, 192, 33), (32, 640, 4096), (17, 12288, 96)])
+def test_few_rows_ragged_shapes(M, K, Nout):
+    """Few-row launches with fewer slabs than stages (K = 64, 192), a ragged
+    last column block, 17 rows (32 staged rows) and a long K (12,288): gated
+    outputs match the oracle and equal the tiled kernel's rows bit for bit."""
+    x, W, A, B, mask = case(10, 256, K, Nout, 32)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    full = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=0.75)
+    few = dvd.isd_linear_gated(xd[:M].contiguous(), Wd, Ad, Bd, md[:M].contiguous(), scale=0.75)
+    torch.cuda.synchronize()
+    assert torch.equal(few.view(torch.int32), full[:M].view(torch.int32))
+    want = ref.gated_lora(x[:M].double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(),
+                          mask[:M], 0.75)
+    assert rel_err(few.cpu().double().numpy(), want) < 2e-3
