@@ -115,10 +115,9 @@ def committed_traffic():
     return rec
 
 
-def summarize_counters(root):
-    """Per-kernel mean of every counter in a rocprofv3 --pmc CSV output tree
-    (KiB per dispatch for FETCH_SIZE / WRITE_SIZE), one line per kernel and
-    counter."""
+def counter_means(root):
+    """{(kernel, counter): [values per dispatch]} from a rocprofv3 --pmc CSV
+    output tree."""
     import collections
     import csv
     acc = collections.defaultdict(list)
@@ -128,7 +127,64 @@ def summarize_counters(root):
                 with open(os.path.join(dirpath, f)) as fh:
                     for row in csv.DictReader(fh):
                         acc[(row["Kernel_Name"], row["Counter_Name"])].append(float(row["Counter_Value"]))
-    for (k, c), v in sorted(acc.items()):
+    return acc
+
+
+def short_kernel(name):
+    name = name.split("(")[0].replace("unsigned short", "bf16")
+    return name[5:] if name.startswith("void ") else name
+
+
+def traffic_report(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, algo_json):
+    """HBM bytes per dispatch of the step's kernels from FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
+    reads for a plain 1 GiB device copy, against the algorithmic bytes the
+    profiled run recorded (--algo-out). Prints a markdown report ending in a
+    RESULT line for the attention call."""
+    fetch, write = counter_means(fetch_dir), counter_means(write_dir)
+    cf, cw = counter_means(copy_fetch_dir), counter_means(copy_write_dir)
+    algo = json.load(open(algo_json))
+    copied_kib = algo["copy_probe_bytes"] / 1024
+
+    def copy_factor(acc, counter):
+        vals = [v for (k, c), vs in acc.items() if c == counter and "copy" in k.lower() for v in vs]
+        return copied_kib / (sum(vals) / len(vals))
+
+    ff, fw = copy_factor(cf, "FETCH_SIZE"), copy_factor(cw, "WRITE_SIZE")
+    print(f"- FETCH_SIZE scale: {ff:.5f} (a 1 GiB copy reads {copied_kib / ff:.0f} KiB)")
+    print(f"- WRITE_SIZE scale: {fw:.5f} (a 1 GiB copy writes {copied_kib / fw:.0f} KiB)\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) |")
+    print("|---|---|---|---|---|")
+    per = {}
+    for (k, c), vs in sorted(fetch.items()):
+        if c != "FETCH_SIZE":
+            continue
+        wv = write.get((k, "WRITE_SIZE"), [0.0])
+        f_kib, w_kib = sum(vs) / len(vs), sum(wv) / len(wv)
+        mb = (f_kib * ff + w_kib * fw) * 1024 / 1e6
+        per[short_kernel(k)] = (len(vs), f_kib, w_kib, mb)
+        print(f"| `{short_kernel(k)}` | {len(vs)} | {f_kib:.1f} | {w_kib:.1f} | {mb:.2f} |")
+    att = [v for k, v in per.items() if k.startswith("isd::attention_kernel") or k.startswith("isd::attention_merge")]
+    call_bytes = sum(v[3] for v in att) * 1e6
+    algo_call = float(np.mean(algo["attention_bytes_per_step"]))
+    print(f"\n- isd_attention call (main + merge): {call_bytes / 1e9:.4f} GB per call; algorithmic "
+          f"{algo_call / 1e9:.4f} GB (ratio {call_bytes / algo_call:.4f})")
+    acc_k = [v for k, v in per.items() if k.startswith("isd::accept_")]
+    if acc_k:
+        acc_bytes = sum(v[3] for v in acc_k) * 1e6
+        algo_acc = float(np.mean(algo["accept_bytes_per_step"]))
+        print(f"- isd_accept step: {acc_bytes / 1e6:.1f} MB per step; algorithmic {algo_acc / 1e6:.1f} MB "
+              f"(ratio {acc_bytes / algo_acc:.4f})")
+    rec = {"kernel_source_sha256": kernel_source_hash(), "hbm_bytes_per_call": int(call_bytes),
+           "algorithmic_bytes_per_call": int(algo_call), "ratio_to_algorithmic": round(call_bytes / algo_call, 4)}
+    print("\nRESULT " + json.dumps(rec))
+
+
+def summarize_counters(root):
+    """Per-kernel mean of every counter in a rocprofv3 --pmc CSV output tree
+    (KiB per dispatch for FETCH_SIZE / WRITE_SIZE), one line per kernel and
+    counter."""
+    for (k, c), v in sorted(counter_means(root).items()):
         print(f"{c:28s} dispatches={len(v):5d} mean={sum(v) / len(v):.6g}  {k[:90]}")
 
 
@@ -528,7 +584,16 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print per-kernel means of a rocprofv3 --pmc CSV output directory and exit")
+    ap.add_argument("--algo-out", metavar="FILE",
+                    help="write the algorithmic bytes of every step's attention call and accept to FILE (JSON)")
+    ap.add_argument("--traffic-report", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR", "ALGO_JSON"),
+                    help="HBM traffic report from FETCH_SIZE / WRITE_SIZE counter runs of the step and of "
+                         "--copy-probe, against the --algo-out bytes of the profiled run, and exit")
     args = ap.parse_args()
+    if args.traffic_report:
+        traffic_report(*args.traffic_report)
+        return
     if args.slices is None:
         # The chunk size is a deployment constant picked for the context mix:
         # at 16,384-token contexts, 66 tiles give 8 chunks per sequence and
@@ -713,6 +778,11 @@ def main():
     assert err.item() == 0, f"device error flags {err.item()}"
     assert np.array_equal(ctx_end, final_ctx), "timed run diverged from the fixed trajectory"
     tokens = int(np.sum(ctx_end - ctx_start))  # n_emit == kv_commit per sequence-step
+    if args.algo_out:
+        with open(args.algo_out, "w") as fh:
+            json.dump({"attention_bytes_per_step": [attention_bytes(ctxs[t], cfg) for t in range(total)],
+                       "accept_bytes_per_step": [accept_bytes(nds[t], accs[t], cfg) for t in range(total)],
+                       "layers": L, "copy_probe_bytes": 2 * (1 << 29)}, fh)
 
     att_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in att_ev])  # [K, L]
     qkv_ms = np.array([[a.elapsed_time(b) for a, b, _ in row] for row in proj_ev])
