@@ -483,7 +483,7 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=
         cores = os.cpu_count()
     C, N, Hq, Hkv, D, V = cfg["C"], cfg["N"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["V"]
     R, H, r = 2 * N, cfg["hidden"], cfg["lora_rank"]
-    ctxs = workload.contexts(cfg["seed"], C, cfg["ctx"])[:fwd_seqs]
+    ctxs = workload.contexts(cfg["seed"], max(C, fwd_seqs), cfg["ctx"])[:fwd_seqs]
     L = cfg["layers"]
     Lt = layers_timed or L
 
@@ -886,7 +886,7 @@ def main():
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
         res["cpu_baseline"] = {"8b": lambda: cpu_baseline(cfg),
-                               "8b1": lambda: cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14),
+                               "8b1": lambda: cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14),
                                "32b": lambda: cpu_baseline(cfg, fwd_seqs=1, accept_seqs=16, accept_steps=14,
                                                            layers_timed=8)}[args.workload]()
         log(f"[bench] cpu baseline took {time.perf_counter() - t_cpu:.1f} s")
