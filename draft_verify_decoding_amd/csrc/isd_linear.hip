@@ -493,7 +493,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 // the tiled kernel's swizzled LDS layout. Each 32x32 output block runs the
 // tiled kernel's MFMA sequence, the same instruction on the same operands
 // slab by slab in ascending K, and the gated epilogue is the tiled
-// kernel's: every output has the bits the tiled kernel gives it.
+// kernel's: every output has the bits the tiled kernel gives it. A split-K
+// launch (U = x A^T's partials) runs each split's share of the slabs, as
+// the tiled kernel does.
 template <int AL>
 struct SkinnyShape {
   static constexpr int kLoads = AL + 4;  // 1 KB direct loads per slab
@@ -570,9 +572,13 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
   };
 
-  const int nk = p.K / kBK;
+  // split-K (U's partials): split blockIdx.y runs the tiled kernel's share
+  // of the slabs, [s nk / splits, (s+1) nk / splits), into its own output
+  const int split = blockIdx.y;
+  const int nk_all = p.K / kBK;
+  const int kb = split * nk_all / p.splits, nk = (split + 1) * nk_all / p.splits - kb;
 #pragma unroll
-  for (int d = 0; d < S - 1; ++d) load_slab(min(d, nk - 1) * kBK, d);
+  for (int d = 0; d < S - 1; ++d) load_slab((kb + min(d, nk - 1)) * kBK, d);
 
   // Gated: while the first slabs are in flight, the U rows (split-K
   // partials summed in split order, as the tiled kernel sums them) go to
@@ -612,7 +618,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
       // flight, and the reads of slab kt-1's stage (the one the next load
       // overwrites) are done once no LDS operation is
       wait_vm_lgkm0<(S - 2) * kLoads>();
-      load_slab(min(kt + S - 1, nk - 1) * kBK, (d + S - 1) % S);
+      load_slab((kb + min(kt + S - 1, nk - 1)) * kBK, (d + S - 1) % S);
       compute(d);
     }
   }
@@ -628,11 +634,12 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
     if (__any(live)) dl = lora_delta<R16>(u_frag<R16>(lane32 < p.M ? &s_u[lane32 * kUStride] : nullptr, hh), bfr);
   }
   const int col = n0 + lane32;
+  float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
     if (row < p.M && col < p.Nout)
-      p.y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e];
+      y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e];
   }
 }
 
@@ -729,15 +736,15 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
       pick = i;
     }
   }
-  if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
-    if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
-  if (p.splits == 1 && p.M <= 32) {  // few rows: one wave per 32 output columns
-    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32));
+  if (p.M <= 32 && (R16 == 0 || p.splits == 1)) {  // few rows: one wave per 32 output columns (and split)
+    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32), static_cast<unsigned>(p.splits));
     if (p.M <= 8) hipLaunchKernelGGL((gemm_skinny_kernel<1, R16>), grid, dim3(64), 0, stream, p);
     else if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<2, R16>), grid, dim3(64), 0, stream, p);
     else hipLaunchKernelGGL((gemm_skinny_kernel<4, R16>), grid, dim3(64), 0, stream, p);
     return hipGetLastError();
   }
+  if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
+    if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
   switch (pick) {
     case 0: return launch_tile<2, 3, 3, R16>(p, stream);
     case 1: return launch_tile<1, 3, 4, R16>(p, stream);
