@@ -532,6 +532,9 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
 
   const int lane = threadIdx.x, lane32 = lane & 31, hh = lane >> 5;
   const int n0 = blockIdx.x * 32;
+  // rows m0 .. m0+31 (blockIdx.z > 0 only for the ungated split-K partials;
+  // the gated epilogue runs with M <= 32, one row block)
+  const int m0 = blockIdx.z * 32;
   // Load q of a slab fills 8 LDS rows, lane i row i / 8 at slot i % 8,
   // with the chunk the swizzle puts there (chunk c of row r sits at slot
   // c ^ (r % 8) ^ ((r / 8) % 2)). x rows past M read row M - 1 and W rows
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
   const uint16_t* b_src[4];
 #pragma unroll
   for (int q = 0; q < AL; ++q)
-    a_src[q] = p.x + static_cast<long>(min(8 * q + g_row, p.M - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
+    a_src[q] = p.x + static_cast<long>(min(m0 + 8 * q + g_row, p.M - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     b_src[q] = p.w + static_cast<long>(min(n0 + 8 * q + g_row, p.Nout - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
@@ -637,7 +640,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
   float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
+    const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
     if (row < p.M && col < p.Nout)
       y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e];
   }
@@ -736,15 +739,18 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
       pick = i;
     }
   }
-  if (p.M <= 32 && (R16 == 0 || p.splits == 1)) {  // few rows: one wave per 32 output columns (and split)
-    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32), static_cast<unsigned>(p.splits));
-    if (p.M <= 8) hipLaunchKernelGGL((gemm_skinny_kernel<1, R16>), grid, dim3(64), 0, stream, p);
+  // Few rows: one wave per 32 output columns (and split). The ungated
+  // split-K partials of U run here at any M, one wave per 32 x 32 output
+  // block and split: each wave keeps all of its split's slabs in flight.
+  if (p.M <= 32 || (R16 == 0 && p.splits > 1)) {
+    const unsigned mblocks = R16 == 0 ? static_cast<unsigned>((p.M + 31) / 32) : 1u;
+    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32), static_cast<unsigned>(p.splits), mblocks);
+    if (mblocks > 1) hipLaunchKernelGGL((gemm_skinny_kernel<4, R16>), grid, dim3(64), 0, stream, p);
+    else if (p.M <= 8) hipLaunchKernelGGL((gemm_skinny_kernel<1, R16>), grid, dim3(64), 0, stream, p);
     else if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<2, R16>), grid, dim3(64), 0, stream, p);
     else hipLaunchKernelGGL((gemm_skinny_kernel<4, R16>), grid, dim3(64), 0, stream, p);
     return hipGetLastError();
   }
-  if constexpr (R16 == 0)  // split-K U partials: many short workgroups, three per CU
-    if (p.splits > 1) return launch_tile<1, 1, 3, 0>(p, stream);
   switch (pick) {
     case 0: return launch_tile<2, 3, 3, R16>(p, stream);
     case 1: return launch_tile<1, 3, 4, R16>(p, stream);
