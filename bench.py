@@ -856,6 +856,7 @@ def main():
         "accept_ms_per_step": round(float(acc_ms.mean()), 5),
         "kv_commit_ms_per_step": round(float(com_ms.mean()), 5) if com_ms is not None else None,
         "accept_gbps": round(acc_gbps, 1),
+        "accept_frac_of_peak": round(acc_gbps / HBM_PEAK_GBPS, 4),
         "attn_accept_gbps": round(aa_gbps, 1),
         "attn_accept_frac_of_peak": round(aa_gbps / HBM_PEAK_GBPS, 4),
         "attn_accept_only_tokens_per_s": round(float(att_only_tps), 1),
