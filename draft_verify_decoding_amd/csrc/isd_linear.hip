@@ -494,8 +494,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 // tiled kernel's MFMA sequence, the same instruction on the same operands
 // slab by slab in ascending K, and the gated epilogue is the tiled
 // kernel's: every output has the bits the tiled kernel gives it. A split-K
-// launch (U = x A^T's partials) runs each split's share of the slabs, as
-// the tiled kernel does.
+// launch (U = x A^T's partials, at any M: one wave per 32x32 block and
+// split, blockIdx.z the 32-row block) runs each split's share of the
+// slabs, as the tiled kernel does.
 template <int AL>
 struct SkinnyShape {
   static constexpr int kLoads = AL + 4;  // 1 KB direct loads per slab
