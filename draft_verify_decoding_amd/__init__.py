@@ -105,15 +105,16 @@ _SIGNATURES = {
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p]),
     "isd_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_void_p, ctypes.c_void_p]),
+                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "isd_lora_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int]),
     "gated_lora_apply": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
     "isd_linear_gated": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                        ctypes.c_void_p]),
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
     "isd_rmsnorm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
     "isd_cast_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -377,12 +378,13 @@ def isd_block_assemble(state, emit, n_emit, ctx, N, mask_id, tokens=None, positi
 
 
 # --------------------------------------------------------------- projections
-def isd_linear(x, W, y=None, stream=None):
+def isd_linear(x, W, y=None, stream=None, ydtype=torch.float32):
+    """y = x W^T; y fp32 or bf16 (`ydtype`, or the dtype of a given y)."""
     M, K = x.shape
     Nout = W.shape[0]
     if y is None:
-        y = torch.empty((M, Nout), dtype=torch.float32, device=x.device)
-    _check(lib().isd_linear(_p(x), _p(W), M, K, Nout, _p(y), _stream(stream)), "isd_linear")
+        y = torch.empty((M, Nout), dtype=ydtype, device=x.device)
+    _check(lib().isd_linear(_p(x), _p(W), M, K, Nout, _p(y), _dtype_code(y), _stream(stream)), "isd_linear")
     return y
 
 
@@ -396,20 +398,20 @@ def gated_lora_apply(x, A, B, is_mask, y, scale=1.0, ws=None, stream=None):
     if ws is None:
         ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
     rc = lib().gated_lora_apply(_p(x), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
-                                _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+                                _dtype_code(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gated_lora_apply")
     return y
 
 
-def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=None):
+def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=None, ydtype=torch.float32):
     M, K = x.shape
     r, Nout = A.shape[0], W.shape[0]
     if y is None:
-        y = torch.empty((M, Nout), dtype=torch.float32, device=x.device)
+        y = torch.empty((M, Nout), dtype=ydtype, device=x.device)
     if ws is None:
         ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
     rc = lib().isd_linear_gated(_p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
-                                _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+                                _dtype_code(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "isd_linear_gated")
     return y
 
@@ -522,13 +524,14 @@ def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, d
 
 def prepare_linear(x, W, y, stream=None):
     M, K = x.shape
-    return Prepared("isd_linear", _p(x), _p(W), M, K, W.shape[0], _p(y), _stream(stream), keep=(x, W, y))
+    return Prepared("isd_linear", _p(x), _p(W), M, K, W.shape[0], _p(y), _dtype_code(y), _stream(stream),
+                    keep=(x, W, y))
 
 
 def prepare_linear_gated(x, W, A, B, is_mask, y, ws, scale=1.0, stream=None):
     M, K = x.shape
     return Prepared("isd_linear_gated", _p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, W.shape[0], A.shape[0],
-                    float(scale), _p(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream),
+                    float(scale), _p(y), _dtype_code(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream),
                     keep=(x, W, A, B, is_mask, y, ws))
 
 

@@ -114,7 +114,8 @@ __device__ __forceinline__ f32x16 lora_delta(const UFrag<R16>& uf, const BFrag<R
 struct GemmParams {
   const uint16_t* x;    // [M][K]
   const uint16_t* w;    // [Nout][K]
-  float* y;             // [splits][M][Nout]
+  void* y;              // [splits][M][Nout]: fp32, or bf16 bits when ybf16
+  int ybf16;            // store y rounded to bf16 (nearest even); never for split-K partials
   // gated epilogue (R16 > 0): MASK rows get y = acc + scale * U B^T
   const float* u;       // U = x A^T as u_splits split-K partials [u_splits][M][r] fp32
   int u_splits;         // summed in split order while staged into LDS
@@ -130,6 +131,15 @@ struct GemmParams {
   int tiles_n;
   int yb_vec;           // rows of yb start 16-byte aligned: store them 16 bytes at a time
 };
+
+// One output element, fp32 or rounded to bf16 (nearest even).
+__device__ __forceinline__ void store_y(void* y, bool ybf16, long i, float v) {
+  if (ybf16) static_cast<uint16_t*>(y)[i] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else static_cast<float*>(y)[i] = v;
+}
+__device__ __forceinline__ float load_y(const void* y, bool ybf16, long i) {
+  return ybf16 ? bf16_lo(static_cast<const uint16_t*>(y)[i]) : static_cast<const float*>(y)[i];
+}
 
 // Wait until at most n vector-memory operations of this wave are in flight
 // and all of its LDS operations are done (exp counter not waited on).
@@ -450,7 +460,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   // Epilogue: register e of lane (j, hh) is row 8(e/4) + 4hh + e%4 of the
   // 32x32 block, column j. Gated: a MASK row takes acc + scale * delta, a
   // clean row takes acc itself.
-  float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
+  void* const y = p.ybf16 ? static_cast<void*>(static_cast<uint16_t*>(p.y) + static_cast<long>(split) * p.M * p.Nout)
+                           : static_cast<void*>(static_cast<float*>(p.y) + static_cast<long>(split) * p.M * p.Nout);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m0 = m_blk + wm + 32 * i;
@@ -477,7 +488,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
         if (row < p.M && col < p.Nout)
-          y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[i][j][e]) : acc[i][j][e];
+          store_y(y, p.ybf16, static_cast<long>(row) * p.Nout + col,
+                  ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[i][j][e]) : acc[i][j][e]);
       }
     }
   }
@@ -638,12 +650,14 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
     if (__any(live)) dl = lora_delta<R16>(u_frag<R16>(lane32 < p.M ? &s_u[lane32 * kUStride] : nullptr, hh), bfr);
   }
   const int col = n0 + lane32;
-  float* y = p.y + static_cast<long>(split) * p.M * p.Nout;
+  void* const y = p.ybf16 ? static_cast<void*>(static_cast<uint16_t*>(p.y) + static_cast<long>(split) * p.M * p.Nout)
+                           : static_cast<void*>(static_cast<float*>(p.y) + static_cast<long>(split) * p.M * p.Nout);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
     if (row < p.M && col < p.Nout)
-      y[static_cast<long>(row) * p.Nout + col] = ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e];
+      store_y(y, p.ybf16, static_cast<long>(row) * p.Nout + col,
+              ((live >> e) & 1) ? fmaf(p.scale, dl[e], acc[e]) : acc[e]);
   }
 }
 
@@ -654,7 +668,8 @@ struct DeltaParams {
   const float* u;      // [M][r]
   const uint16_t* b;   // [Nout][r]
   const uint8_t* mask; // [M]
-  float* y;            // [M][Nout]
+  void* y;             // [M][Nout], fp32 or bf16 bits
+  int ybf16;
   int M, Nout;
   float scale;
 };
@@ -678,7 +693,7 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-    yv[e] = ((live >> e) & 1) ? p.y[static_cast<long>(row) * p.Nout + bcol] : 0.f;
+    yv[e] = ((live >> e) & 1) ? load_y(p.y, p.ybf16, static_cast<long>(row) * p.Nout + bcol) : 0.f;
   }
   const UFrag<R16> uf = u_frag<R16>(m0 + lane32 < p.M ? p.u + static_cast<long>(m0 + lane32) * 16 * R16 : nullptr, hh);
   const f32x16 dl = lora_delta<R16>(uf, b_frag<R16>(p.b, p.Nout, n0, lane32, hh));
@@ -686,7 +701,7 @@ __global__ __launch_bounds__(256) void lora_delta_kernel(DeltaParams p) {
   for (int e = 0; e < 16; ++e) {
     if ((live >> e) & 1) {
       const int row = m0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-      p.y[static_cast<long>(row) * p.Nout + bcol] = fmaf(p.scale, dl[e], yv[e]);
+      store_y(p.y, p.ybf16, static_cast<long>(row) * p.Nout + bcol, fmaf(p.scale, dl[e], yv[e]));
     }
   }
 }
@@ -838,12 +853,13 @@ const float* lora_u_of(void* ws, int M, int r) {
 }
 
 hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int M, int Nout, int r, float scale,
-                        float* y, hipStream_t stream) {
+                        void* y, int ybf16, hipStream_t stream) {
   DeltaParams d{};
   d.u = U;
   d.b = static_cast<const uint16_t*>(B);
   d.mask = mask;
   d.y = y;
+  d.ybf16 = ybf16;
   d.M = M;
   d.Nout = Nout;
   d.scale = scale;
@@ -862,10 +878,12 @@ hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int 
   return hipGetLastError();
 }
 
-int check_gemm_args(const void* x, const void* W, int M, int K, int Nout, const float* y) {
+int check_gemm_args(const void* x, const void* W, int M, int K, int Nout, const void* y, int ydtype) {
   if (M < 0 || K < 0 || Nout < 0) return ISD_E_INVALID;
+  if (ydtype != ISD_F32 && ydtype != ISD_BF16) return ISD_E_UNSUPPORTED;
   if (M == 0 || Nout == 0) return ISD_OK;
   if (!x || !W || !y) return ISD_E_INVALID;
+  if ((reinterpret_cast<uintptr_t>(y) & (ydtype == ISD_F32 ? 3u : 1u)) != 0) return ISD_E_INVALID;
   if (K == 0 || K % kBK != 0) return ISD_E_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(W)) return ISD_E_INVALID;
   return ISD_OK;
@@ -883,8 +901,8 @@ int check_lora_args(const void* A, const void* B, const uint8_t* mask, int r, vo
 
 extern "C" {
 
-int isd_linear(const void* x, const void* W, int M, int K, int Nout, float* y, hipStream_t stream) {
-  int rc = check_gemm_args(x, W, M, K, Nout, y);
+int isd_linear(const void* x, const void* W, int M, int K, int Nout, void* y, int ydtype, hipStream_t stream) {
+  int rc = check_gemm_args(x, W, M, K, Nout, y, ydtype);
   if (rc || M == 0 || Nout == 0) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
@@ -892,6 +910,7 @@ int isd_linear(const void* x, const void* W, int M, int K, int Nout, float* y, h
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
   p.y = y;
+  p.ybf16 = ydtype == ISD_BF16;
   p.M = M;
   p.K = K;
   p.Nout = Nout;
@@ -905,21 +924,23 @@ size_t isd_lora_workspace_size(int M, int r) {
 }
 
 int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t* is_mask, int M, int K, int Nout,
-                     int r, float scale, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_gemm_args(x, A, M, K, Nout, y);
+                     int r, float scale, void* y, int ydtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_gemm_args(x, A, M, K, Nout, y, ydtype);
   if (rc || M == 0 || Nout == 0) return rc;
   rc = check_lora_args(A, B, is_mask, r, ws, ws_bytes, M);
   if (rc) return rc;
   rc = isd_check_device_internal();
   if (rc) return rc;
   if (launch_lora_u(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
-  return launch_delta(lora_u_of(ws, M, r), B, is_mask, M, Nout, r, scale, y, stream) == hipSuccess ? ISD_OK
-                                                                                                   : ISD_E_LAUNCH;
+  return launch_delta(lora_u_of(ws, M, r), B, is_mask, M, Nout, r, scale, y, ydtype == ISD_BF16, stream) == hipSuccess
+             ? ISD_OK
+             : ISD_E_LAUNCH;
 }
 
 int isd_linear_gated(const void* x, const void* W, const void* A, const void* B, const uint8_t* is_mask, int M, int K,
-                     int Nout, int r, float scale, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_gemm_args(x, W, M, K, Nout, y);
+                     int Nout, int r, float scale, void* y, int ydtype, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int rc = check_gemm_args(x, W, M, K, Nout, y, ydtype);
   if (rc || M == 0 || Nout == 0) return rc;
   rc = check_lora_args(A, B, is_mask, r, ws, ws_bytes, M);
   if (rc) return rc;
@@ -932,6 +953,7 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
   p.y = y;
+  p.ybf16 = ydtype == ISD_BF16;
   p.u = static_cast<const float*>(ws);
   p.u_splits = u_splits(K);
   p.b = static_cast<const uint16_t*>(B);

@@ -15,7 +15,7 @@
  *   isd_kv_write_layers  isd_kv_write for every layer of a model in one launch
  *   isd_accept        vocab softmax, p/q test, residual / bonus draw, proposals
  *   isd_block_assemble  the next step's block: newest token, drafts, MASK
- *   isd_linear        y = x W^T (bf16 in, fp32 out), the base projection
+ *   isd_linear        y = x W^T (bf16 in, fp32 or bf16 out), the base projection
  *   gated_lora_apply  y += s (x A^T) B^T on MASK rows only (R-ISD)
  *   isd_linear_gated  both of the above in one pass
  *   isd_lm_head       logits = h W^T (bf16) with their softmax chunk statistics
@@ -329,9 +329,10 @@ int isd_block_assemble(const isd_seq_state* st, const int32_t* emit,
  * Lossless R-ISD": the adapter acts only at MASK positions so clean
  * positions stay bit-identical to the base model).
  *
- * isd_linear: y[M][Nout] (fp32) = x[M][K] W[Nout][K]^T with bf16 x and W.
- * Each output's reduction order depends only on K, never on M, on the other
- * rows or on their mask.
+ * isd_linear: y[M][Nout] = x[M][K] W[Nout][K]^T with bf16 x and W,
+ * accumulated in fp32; y is fp32 (ydtype ISD_F32) or the fp32 value rounded
+ * to bf16, nearest even (ISD_BF16). Each output's reduction order depends
+ * only on K, never on M, on the other rows or on their mask.
  * gated_lora_apply: y[m] += scale * (x[m] A^T) B^T for rows with
  * is_mask[m] != 0; A [r][K] and B [Nout][r] bf16; other rows are never
  * written. U = x A^T (fp32, a split-K GEMM whose split count depends on K
@@ -340,24 +341,28 @@ int isd_block_assemble(const isd_seq_state* st, const int32_t* emit,
  * contents on entry ignored).
  * isd_linear_gated: y = isd_linear(x, W) then gated_lora_apply, with the
  * delta added in the base GEMM's epilogue; its clean rows equal isd_linear's
- * bit for bit and its MASK rows equal those of the two separate calls.
+ * bit for bit and, with fp32 y, its MASK rows equal those of the two
+ * separate calls. With bf16 y, gated_lora_apply reads y, adds the delta in
+ * fp32 and rounds again, so the separate calls' MASK rows carry a second
+ * rounding that the fused call does not.
  * x, W, A, B must be 16-byte aligned, all row-major and contiguous.
- * Supported: K multiple of 64; r multiple of 16, <= 128. M == 0 or Nout == 0
- * returns ISD_OK with nothing launched. Errors: ISD_E_INVALID (null or
- * misaligned pointer, negative size), ISD_E_UNSUPPORTED (K, r), and
- * ISD_E_WORKSPACE; nothing is launched on an error.
+ * Supported: K multiple of 64; r multiple of 16, <= 128; ydtype ISD_F32 or
+ * ISD_BF16 (y 4- or 2-byte aligned). M == 0 or Nout == 0 returns ISD_OK with
+ * nothing launched. Errors: ISD_E_INVALID (null or misaligned pointer,
+ * negative size), ISD_E_UNSUPPORTED (K, r, ydtype), and ISD_E_WORKSPACE;
+ * nothing is launched on an error.
  */
 int isd_linear(const void* x, const void* W, int M, int K, int Nout,
-               float* y, hipStream_t stream);
+               void* y, int ydtype, hipStream_t stream);
 size_t isd_lora_workspace_size(int M, int r);
 int gated_lora_apply(const void* x, const void* A, const void* B,
                      const uint8_t* is_mask, int M, int K, int Nout, int r,
-                     float scale, float* y, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     float scale, void* y, int ydtype, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 int isd_linear_gated(const void* x, const void* W, const void* A,
                      const void* B, const uint8_t* is_mask, int M, int K,
-                     int Nout, int r, float scale, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t stream);
+                     int Nout, int r, float scale, void* y, int ydtype,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ LM head
  * The distributions the accept step compares are the softmax of the

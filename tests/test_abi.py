@@ -144,13 +144,18 @@ def test_accept_rejects_bad_arguments_on_host(lib):
 
 
 def test_linear_rejects_bad_arguments_on_host(lib):
-    assert lib.isd_linear(16, 16, 4, 100, 8, 16, None) == -2  # K not a multiple of 64
-    assert lib.isd_linear(None, 16, 4, 64, 8, 16, None) == -1
-    assert lib.isd_linear(16, 16, 0, 64, 8, 16, None) == 0  # empty problem
-    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, 16, 1 << 20, None) == -2  # rank 24
-    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 16, 8, None) == -3  # ws too small
+    F32, BF16 = dvd.ISD_F32, dvd.ISD_BF16
+    assert lib.isd_linear(16, 16, 4, 100, 8, 16, F32, None) == -2  # K not a multiple of 64
+    assert lib.isd_linear(None, 16, 4, 64, 8, 16, F32, None) == -1
+    assert lib.isd_linear(16, 16, 0, 64, 8, 16, F32, None) == 0  # empty problem
+    assert lib.isd_linear(16, 16, 4, 64, 8, 16, 7, None) == -2  # output type
+    assert lib.isd_linear(16, 16, 4, 64, 8, 18, F32, None) == -1  # fp32 output not 4-byte aligned
+    assert lib.isd_linear(16, 16, 4, 64, 8, 17, BF16, None) == -1  # bf16 output not 2-byte aligned
+    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, F32, 16, 1 << 20, None) == -2  # rank 24
+    assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, F32, 16, 8, None) == -3  # ws too small
     assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4 * 9  # 8 split-K partials of U, then U
-    assert lib.gated_lora_apply(16, 16, 24, 16, 4, 64, 8, 32, 1.0, 16, 16, 512, None) == -1  # B misaligned
+    assert lib.gated_lora_apply(16, 16, 24, 16, 4, 64, 8, 32, 1.0, 16, F32, 16, 512, None) == -1  # B misaligned
+    assert lib.isd_linear_gated(16, 16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 0, 16, 1 << 20, None) == -2  # type
 
 
 def test_block_assemble_rejects_bad_arguments_on_host(lib):

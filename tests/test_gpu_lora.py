@@ -227,3 +227,36 @@ def test_few_rows_ragged_shapes(M, K, Nout):
     want = ref.gated_lora(x[:M].double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(),
                           mask[:M], 0.75)
     assert rel_err(few.cpu().double().numpy(), want) < 2e-3
+
+
+@pytest.mark.parametrize("M", [8, 512])
+def test_bf16_output_is_the_rounded_fp32_output(M):
+    """ydtype bf16: every output is the fp32 result rounded to nearest even,
+    in the tiled kernel (512 rows) and the few-row kernel (8 rows), base and
+    fused gated; clean rows of the gated call equal the base call's; the
+    separate gated_lora_apply on a bf16 y rounds its MASK rows a second time,
+    so they stay within one bf16 step of the fused call's."""
+    x, W, A, B, mask = case(11, M, 4096, 4096, 32)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    base32 = dvd.isd_linear(xd, Wd)
+    base16 = dvd.isd_linear(xd, Wd, ydtype=torch.bfloat16)
+    fused32 = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=1.0)
+    fused16 = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=1.0, ydtype=torch.bfloat16)
+    sep16 = base16.clone()
+    dvd.gated_lora_apply(xd, Ad, Bd, md, sep16, scale=1.0)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16)
+    assert base16.dtype == torch.bfloat16 and fused16.dtype == torch.bfloat16
+    assert torch.equal(bits(base16), bits(base32.to(torch.bfloat16)))
+    assert torch.equal(bits(fused16), bits(fused32.to(torch.bfloat16)))
+    m = torch.from_numpy(mask).to(DEV)
+    assert torch.equal(bits(fused16[~m]), bits(base16[~m]))
+    assert torch.equal(bits(sep16[~m]), bits(base16[~m]))
+    # the separate call rounds the base value before adding the delta: the
+    # two differ by at most a rounding of the base value and one of each result
+    f, s_, acc = fused16[m].float(), sep16[m].float(), base32[m]
+    assert torch.all((f - s_).abs() <= 2.0 ** -8 * (acc.abs() + f.abs() + s_.abs()) + 1e-30)
+    want = ref.gated_lora(x.double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(), mask, 1.0)
+    got = fused16.float().cpu().double().numpy()
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-4 * np.abs(want).max())
