@@ -86,13 +86,13 @@ _SIGNATURES = {
                                                        ctypes.POINTER(IsdKvCache), ctypes.c_int, ctypes.c_int]),
     "isd_attention": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
-                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p, ctypes.c_void_p]),
     "isd_attention_with_block": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
-                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                                ctypes.c_void_p]),
+                                                ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                ctypes.c_void_p, ctypes.c_void_p]),
     "isd_kv_write_layers": (ctypes.c_int, [ctypes.POINTER(IsdKvCache), ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
@@ -237,15 +237,16 @@ def isd_attention_workspace_size(kv, C, rows, num_q_heads, max_len, slices=0):
 
 
 def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, dev_err=None, stream=None,
-                  k_blk=None, v_blk=None):
-    """out [C, rows, Hq, D] fp32 = causal attention of q over the pages; with
-    k_blk, v_blk ([C, rows, Hkv, D]) the block's own keys come from those rows
+                  k_blk=None, v_blk=None, odtype=torch.float32):
+    """out [C, rows, Hq, D] (fp32, or bf16: `odtype` or the dtype of a given
+    out) = causal attention of q over the pages; with k_blk, v_blk
+    ([C, rows, Hkv, D]) the block's own keys come from those rows
     (isd_attention_with_block)."""
     C, rows, Hq, D = q.shape
     if scale is None:
         scale = D ** -0.5
     if out is None:
-        out = torch.empty((C, rows, Hq, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((C, rows, Hq, D), dtype=odtype, device=q.device)
     need = isd_attention_workspace_size(kv, C, rows, Hq, max_len, slices)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -253,12 +254,13 @@ def isd_attention(kv, q, ctx, max_len, scale=None, slices=0, out=None, ws=None, 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     if k_blk is None:
         rc = lib().isd_attention(ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
-                                 int(slices), _p(out), _p(ws), nbytes, _p(dev_err), _stream(stream))
+                                 int(slices), _p(out), _dtype_code(out), _p(ws), nbytes, _p(dev_err),
+                                 _stream(stream))
         _check(rc, "isd_attention")
     else:
         rc = lib().isd_attention_with_block(ctypes.byref(s), _p(k_blk), _p(v_blk), _p(q), _p(ctx), C, rows, Hq,
-                                            float(scale), int(max_len), int(slices), _p(out), _p(ws), nbytes,
-                                            _p(dev_err), _stream(stream))
+                                            float(scale), int(max_len), int(slices), _p(out), _dtype_code(out),
+                                            _p(ws), nbytes, _p(dev_err), _stream(stream))
         _check(rc, "isd_attention_with_block")
     return out
 
@@ -515,10 +517,10 @@ def prepare_attention(kv, q, ctx, max_len, out, ws=None, slices=0, scale=None, d
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     if k_blk is not None:
         return Prepared("isd_attention_with_block", ctypes.byref(s), _p(k_blk), _p(v_blk), _p(q), _p(ctx), C, rows,
-                        Hq, float(scale), int(max_len), int(slices), _p(out), _p(ws), nbytes, _p(dev_err),
-                        _stream(stream), keep=(s, kv, k_blk, v_blk, q, ctx, out, ws, dev_err))
+                        Hq, float(scale), int(max_len), int(slices), _p(out), _dtype_code(out), _p(ws), nbytes,
+                        _p(dev_err), _stream(stream), keep=(s, kv, k_blk, v_blk, q, ctx, out, ws, dev_err))
     return Prepared("isd_attention", ctypes.byref(s), _p(q), _p(ctx), C, rows, Hq, float(scale), int(max_len),
-                    int(slices), _p(out), _p(ws), nbytes, _p(dev_err), _stream(stream),
+                    int(slices), _p(out), _dtype_code(out), _p(ws), nbytes, _p(dev_err), _stream(stream),
                     keep=(s, kv, q, ctx, out, ws, dev_err))
 
 

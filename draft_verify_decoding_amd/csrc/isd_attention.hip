@@ -51,7 +51,8 @@ struct AttnParams {
   const int32_t* block_table;
   const void* q;
   const int32_t* ctx;
-  float* out;
+  void* out;         // [C][rows][Hq][D], fp32, or bf16 bits when obf16
+  int obf16;        // outputs rounded to bf16 (nearest even); partials stay fp32
   float* part_o;    // [groups * G][2 slots][HPW * MB][32][D]
   float* part_ml;   // same, [2]: (max, sum)
   int32_t* tile_off;  // [C + 1] tile offsets written for the merge launch
@@ -684,10 +685,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     const float l_tot = l_run + shfl_xor_f(l_run, 32);
     const bool whole = kChunked ? c_units == 1 : lt0 == 0 && lt1 == nt;
     if (qvalid) {
-      float* dst;
+      float* dst = nullptr;
       float mul;
+      const size_t oidx = ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
       if (whole) {
-        dst = p.out + ((static_cast<size_t>(b) * p.rows + irow) * p.Hq + h) * D;
+        if (!p.obf16) dst = static_cast<float*>(p.out) + oidx;
         mul = 1.f / l_tot;
       } else {
         // partial piece of this wave's query columns
@@ -709,7 +711,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = o[nb][4 * q4 + e] * mul;
-          *reinterpret_cast<f32x4*>(dst + nb * 32 + 8 * q4 + 4 * hh) = v;
+          if (dst) {
+            *reinterpret_cast<f32x4*>(dst + nb * 32 + 8 * q4 + 4 * hh) = v;
+          } else {  // a whole piece into bf16 outputs: four values, one 8-byte store
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + oidx + nb * 32 + 8 * q4 + 4 * hh) =
+                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+          }
         }
     }
   }
@@ -812,14 +820,19 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p) {
   else merge_all(std::integral_constant<int, kBatch>{});
   const int hl = col / p.rows, i = col % p.rows;
   const int h = g * p.group + hl;
-  f32x4* dst = reinterpret_cast<f32x4*>(p.out + ((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d0);
+  const size_t oidx = ((static_cast<size_t>(b) * p.rows + i) * p.Hq + h) * D + d0;
   const float inv = 1.f / l_run;
 #pragma unroll
   for (int k = 0; k < kV; ++k) {
     f32x4 v = acc[k];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * inv;
-    dst[k] = v;
+    if (p.obf16)
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + oidx)[k] =
+          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+    else
+      reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oidx)[k] = v;
   }
 }
 
@@ -1003,8 +1016,8 @@ hipError_t launch_attention_typed(const AttnParams& p, int groups, hipStream_t s
 // the bodies of isd_attention / isd_attention_with_block and of
 // isd_kv_write / isd_kv_write_layers
 int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk, const void* q, const int32_t* ctx,
-                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, float* out, void* ws,
-                   size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
+                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, void* out, int odtype,
+                   void* ws, size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
 
 int kv_write_call(const isd_kv_cache* kv, int layers, int64_t layer_stride, const void* k, const void* v,
                   const int32_t* pos0, const int32_t* nrows, int C, int rows, int32_t* dev_err, hipStream_t stream) {
@@ -1058,19 +1071,19 @@ size_t isd_attention_workspace_size(int C, int rows, int num_q_heads, const isd_
 }
 
 int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx, int C, int rows, int num_q_heads,
-                  float scale, int max_len, int slices, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
-                  hipStream_t stream) {
-  return attention_call(kv, nullptr, nullptr, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, ws, ws_bytes,
-                        dev_err, stream);
+                  float scale, int max_len, int slices, void* out, int odtype, void* ws, size_t ws_bytes,
+                  int32_t* dev_err, hipStream_t stream) {
+  return attention_call(kv, nullptr, nullptr, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, odtype, ws,
+                        ws_bytes, dev_err, stream);
 }
 
 int isd_attention_with_block(const isd_kv_cache* kv, const void* k, const void* v, const void* q,
                              const int32_t* ctx, int C, int rows, int num_q_heads, float scale, int max_len, int slices,
-                             float* out, void* ws, size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
+                             void* out, int odtype, void* ws, size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
   if (!k || !v) return ISD_E_INVALID;
   if (!aligned16(k) || !aligned16(v)) return ISD_E_INVALID;
-  return attention_call(kv, k, v, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, ws, ws_bytes, dev_err,
-                        stream);
+  return attention_call(kv, k, v, q, ctx, C, rows, num_q_heads, scale, max_len, slices, out, odtype, ws, ws_bytes,
+                        dev_err, stream);
 }
 
 }  // extern "C"
@@ -1078,10 +1091,11 @@ int isd_attention_with_block(const isd_kv_cache* kv, const void* k, const void* 
 namespace {
 
 int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk, const void* q, const int32_t* ctx,
-                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, float* out, void* ws,
-                   size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
+                   int C, int rows, int num_q_heads, float scale, int max_len, int slices, void* out, int odtype,
+                   void* ws, size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
   int rc = check_kv(kv);
   if (rc) return rc;
+  if (odtype != ISD_F32 && odtype != ISD_BF16) return ISD_E_UNSUPPORTED;
   if (C == 0) return ISD_OK;
   if (!q || !ctx || !out) return ISD_E_INVALID;
   if (!(scale > 0.f) || !(scale < INFINITY)) return ISD_E_INVALID;
@@ -1100,6 +1114,7 @@ int attention_call(const isd_kv_cache* kv, const void* k_blk, const void* v_blk,
   p.q = q;
   p.ctx = ctx;
   p.out = out;
+  p.obf16 = odtype == ISD_BF16;
   char* w = static_cast<char*>(ws);
   p.tile_off = reinterpret_cast<int32_t*>(w);
   p.part_o = reinterpret_cast<float*>(w + plan.off_bytes);

@@ -1,6 +1,6 @@
 """A whole synthetic forward of the ISD step through the library: for every
 decoder layer, RMSNorm -> gated Q|K|V projection -> bf16 q, k, v -> causal
-attention of the block over the paged cache -> bf16 -> gated O projection ->
+attention of the block over the paged cache (bf16 out) -> gated O projection ->
 residual add and RMSNorm -> gate|up projection -> SwiGLU -> down projection;
 then the final RMSNorm and the LM head, whose chunk statistics feed the
 accept step. Every step is a library call (argument marshalling only); the
@@ -59,7 +59,8 @@ class Forward:
         self.h = e(M, H)
         self.x, self.x2, self.xf = e(M, H, dt=bf), e(M, H, dt=bf), e(M, H, dt=bf)
         nq = (Hq + 2 * Hkv) * D
-        self.yqkv, self.q, self.att = e(M, nq), e(C, R, Hq, D, dt=bf), e(C, R, Hq, D)
+        self.yqkv, self.q = e(M, nq), e(C, R, Hq, D, dt=bf)
+        # attention writes its bf16 output straight into the O projection's input
         self.ob, self.yo = e(M, Hq * D, dt=bf), e(M, H)
         self.gu, self.act, self.yd = e(M, 2 * I), e(M, I, dt=bf), e(M, H)
         # two logits buffers, alternated step by step: the accept step reads
@@ -74,8 +75,6 @@ class Forward:
         r_max = max([0] + ranks)
         split = layers[0].qkv_adapters is not None
         widths = [Hq * D, Hkv * D, Hkv * D]
-        if split:  # one fp32 output per projection
-            self.yparts = [e(M, wd) for wd in widths]
         self.lora_ws = e(max(isd_lora_workspace_size(M, max(r_max, 16)), 256) // 4)
         need = isd_attention_workspace_size(kvs[0], C, R, Hq, max_len, slices)
         self.att_ws = e(max(need, 256) // 4 + 1)
@@ -85,27 +84,25 @@ class Forward:
         for l, w in enumerate(layers):
             c = self.calls
             c.append(prepare_rmsnorm(self.h, w.g1, self.x, delta=prev_delta))
-            if split:
+            if split:  # each projection rounds its own output to bf16 q, k or v
                 r0 = 0
-                for j, wd in enumerate(widths):
-                    Wj = w.Wqkv[r0:r0 + wd]
+                dsts = (self.q, k_all[l], v_all[l])
+                for j, (wd, dst) in enumerate(zip(widths, dsts)):
+                    Wj, yj = w.Wqkv[r0:r0 + wd], dst.view(M, wd)
                     if lora == "gated":
                         A, B = w.qkv_adapters[j]
-                        c.append(prepare_linear_gated(self.x, Wj, A, B, mask, self.yparts[j], self.lora_ws))
+                        c.append(prepare_linear_gated(self.x, Wj, A, B, mask, yj, self.lora_ws))
                     else:
-                        c.append(prepare_linear(self.x, Wj, self.yparts[j]))
+                        c.append(prepare_linear(self.x, Wj, yj))
                     r0 += wd
-                for y, dst in zip(self.yparts, (self.q, k_all[l], v_all[l])):
-                    c.append(prepare_cast_bf16(y, [dst]))
             else:
                 if lora == "gated":
                     c.append(prepare_linear_gated(self.x, w.Wqkv, w.Aqkv, w.Bqkv, mask, self.yqkv, self.lora_ws))
                 else:
                     c.append(prepare_linear(self.x, w.Wqkv, self.yqkv))
                 c.append(prepare_cast_bf16(self.yqkv, [self.q, k_all[l], v_all[l]]))
-            c.append(prepare_attention(kvs[l], self.q, ctx, max_len, self.att, ws=self.att_ws, slices=slices,
-                                       dev_err=dev_err, k_blk=k_all[l], v_blk=v_all[l]))
-            c.append(prepare_cast_bf16(self.att.view(M, Hq * D), [self.ob]))
+            c.append(prepare_attention(kvs[l], self.q, ctx, max_len, self.ob.view(C, R, Hq, D), ws=self.att_ws,
+                                       slices=slices, dev_err=dev_err, k_blk=k_all[l], v_blk=v_all[l]))
             if lora == "gated":
                 c.append(prepare_linear_gated(self.ob, w.Wo, w.Ao, w.Bo, mask, self.yo, self.lora_ws))
             else:

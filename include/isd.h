@@ -144,7 +144,9 @@ int isd_kv_write_layers(const isd_kv_cache* kv, int layers,
  * have been written with isd_kv_write first.
  *
  *   q    [C][rows][Hq][D] in kv->dtype
- *   out  [C][rows][Hq][D] fp32 (normalised attention output)
+ *   out  [C][rows][Hq][D] normalised attention output: fp32 (odtype
+ *        ISD_F32) or the fp32 value rounded to bf16, nearest even
+ *        (ISD_BF16); 16-byte aligned. Partial results stay fp32.
  *   ctx  [C] cached tokens before the block
  *   Query head h reads KV head h / (Hq / Hkv). scale multiplies q.k
  *   (1/sqrt(D) in the usual model). max_len is a host-side upper bound of
@@ -181,8 +183,8 @@ size_t isd_attention_workspace_size(int C, int rows, int num_q_heads,
                                     int slices);
 int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx,
                   int C, int rows, int num_q_heads, float scale, int max_len,
-                  int slices, float* out, void* ws, size_t ws_bytes,
-                  int32_t* dev_err, hipStream_t stream);
+                  int slices, void* out, int odtype, void* ws,
+                  size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
 
 /* isd_attention_with_block: isd_attention where keys ctx[b] .. ctx[b] +
  * rows - 1, the block's own rows, are read from k and v ([C][rows][Hkv][D]
@@ -198,8 +200,8 @@ int isd_attention(const isd_kv_cache* kv, const void* q, const int32_t* ctx,
 int isd_attention_with_block(const isd_kv_cache* kv, const void* k,
                              const void* v, const void* q, const int32_t* ctx,
                              int C, int rows, int num_q_heads, float scale,
-                             int max_len, int slices, float* out, void* ws,
-                             size_t ws_bytes, int32_t* dev_err,
+                             int max_len, int slices, void* out, int odtype,
+                             void* ws, size_t ws_bytes, int32_t* dev_err,
                              hipStream_t stream);
 
 /* ---------------------------------------------------------- accept

@@ -55,35 +55,37 @@ def test_strerror_and_version(lib):
 
 
 def test_attention_rejects_bad_arguments_on_host(lib):
-    null_kv = lib.isd_attention(None, None, None, 1, 8, 4, 0.1, 64, 0, None, None, 0, None, None)
+    null_kv = lib.isd_attention(None, None, None, 1, 8, 4, 0.1, 64, 0, None, dvd.ISD_F32, None, 0, None, None)
     assert null_kv == -1
     kv = dvd.IsdKvCache(16, 16, 16, 4, 10, 16, 1, 96, dvd.ISD_BF16)  # head_dim 96 unsupported
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -2
     kv.head_dim = 128
     kv.page_size = 8
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -2
     kv.page_size = 16
     # Hq not a multiple of Hkv
     kv.num_kv_heads = 3
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -2
     kv.num_kv_heads = 1
     # group * rows > 128
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 40, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 40, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -2
     # scale must be positive, chunks of the invariant split <= 65536 tiles, max_len >= rows
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, -1.0, 64, 0, 16, None, 0, None, None) == -1
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -65537, 16, None, 0, None, None) == -1
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -3, 16, None, 0, None, None) == -3
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4, 0, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, -1.0, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -65537, 16, dvd.ISD_F32, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, -3, 16, dvd.ISD_F32, None, 0, None, None) == -3
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4, 0, 16, dvd.ISD_F32, None, 0, None, None) == -1
     # misaligned q
-    assert lib.isd_attention(ctypes.byref(kv), 18, 16, 1, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -1
+    assert lib.isd_attention(ctypes.byref(kv), 18, 16, 1, 8, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -1
     # too many sequences for one call
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 9000, 8, 4, 0.1, 64, 0, 16, None, 0, None, None) == -2
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 9000, 8, 4, 0.1, 64, 0, 16, dvd.ISD_F32, None, 0, None, None) == -2
     # the workspace is required and sized by the same arguments
     need = lib.isd_attention_workspace_size(1, 8, 4, ctypes.byref(kv), 4096, 64)
     assert need > 0
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, None, 0, None, None) == -3
-    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, 1 << 20, need - 16, None,
-                             None) == -3
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, dvd.ISD_F32, None, 0, None, None) == -3
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 4096, 64, 16, dvd.ISD_F32, 1 << 20, need - 16,
+                             None, None) == -3
+    # an output type other than fp32 and bf16
+    assert lib.isd_attention(ctypes.byref(kv), 16, 16, 1, 8, 4, 0.1, 64, 0, 16, 9, None, 0, None, None) == -2
 
 
 def test_attention_invariant_split_workspace(lib):

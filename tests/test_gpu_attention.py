@@ -458,3 +458,30 @@ def test_bad_sequences_inside_the_batch_leave_the_others_exact(split):
     kp, vp = oracle_pages(case)
     want = ref.block_attention(to64(case.q)[good], kp, vp, case.table[good], case.ctx[good])
     assert slab_errors(out.cpu().double().numpy()[good], want).max() < 2e-3
+
+
+@pytest.mark.parametrize("slices,with_block", [(0, False), (5, False), (dvd.attn_invariant(1), False),
+                                               (dvd.attn_invariant(2), True), (0, True)])
+def test_bf16_output_is_the_rounded_fp32_output(slices, with_block):
+    """odtype bf16 stores the fp32 result rounded to nearest even, bit for
+    bit, whether a (sequence, head) is finished in the main kernel (one
+    piece) or by the merge of several pieces: contexts from 0 to 700 tokens
+    give both kinds in one call."""
+    case = workload.AttentionCase(73, C=7, rows=8, Hq=32, Hkv=8, D=128, ctx=[0, 1, 31, 64, 129, 300, 700],
+                                  dtype=torch.bfloat16)
+    print(f"attention bf16 output slices={slices} with_block={with_block}", flush=True)
+    kv, err = fill_cache(case)
+    ctx = torch.from_numpy(case.ctx).to(DEV)
+    q = case.q.to(DEV)
+    extra = {}
+    if with_block:
+        extra = dict(zip(("k_blk", "v_blk"), block_rows(case)))
+    max_len = int(case.lengths.max())
+    f32 = dvd.isd_attention(kv, q, ctx, max_len=max_len, slices=slices, dev_err=err, **extra)
+    b16 = dvd.isd_attention(kv, q, ctx, max_len=max_len, slices=slices, dev_err=err, odtype=torch.bfloat16, **extra)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and b16.dtype == torch.bfloat16
+    assert torch.equal(b16.view(torch.int16), f32.to(torch.bfloat16).view(torch.int16))
+    kp, vp = oracle_pages(case)
+    want = ref.block_attention(to64(case.q), kp, vp, case.table, case.ctx)
+    assert slab_errors(b16.cpu().double().numpy(), want).max() < 2e-3 + 2.0 ** -8
