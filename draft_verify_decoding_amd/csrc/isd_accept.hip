@@ -65,8 +65,17 @@ struct AcceptParams {
 };
 
 // --------------------------------------- values handed between workgroups
-// Device-coherent (agent-scope) stores and loads; the writer makes its
-// stores complete (stores_done) before it counts itself in.
+// The residual slices hand their sums to the last slice of their sequence.
+// Each value goes through a device-coherent (agent-scope) store and load,
+// which reach the coherence point of the 8 XCDs directly. The writer waits
+// until its stores are complete (stores_done: s_waitcnt 0, with compiler
+// barriers on both sides) before its relaxed add on the sequence's counter,
+// and the reader issues its loads only after that add has returned the
+// count that makes it last, so no load can see a value older than the
+// store. Release/acquire ordering on the add would also order the stores,
+// but at agent scope gfx950 implements it as a writeback (release) and an
+// invalidation (acquire) of the XCD's L2: a probe of 2,240 counted tasks
+// took 34 us that way against 5 us with relaxed adds.
 __device__ __forceinline__ void stores_done() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
