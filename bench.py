@@ -253,7 +253,7 @@ def build(cfg, steps_total, dev):
                          y=torch.empty((M, H), dtype=torch.float32, device=dev))
         lay["proj"] = proj
         layers.append(lay)
-    lora_ws = torch.empty(dvd.isd_lora_workspace_size(M, 3 * r), dtype=torch.uint8, device=dev)
+    lora_ws = dvd.lora_workspace(M, 3 * r, dev)
     return dict(ctx0=ctx0, kvs=kvs, layer_stride=layer_stride, k_all=k_all, v_all=v_all, layers=layers, mask=mask,
                 lora_ws=lora_ws, table=table)
 

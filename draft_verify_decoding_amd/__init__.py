@@ -394,11 +394,17 @@ def isd_lora_workspace_size(M, r):
     return int(lib().isd_lora_workspace_size(M, r))
 
 
+def lora_workspace(M, r, device="cuda"):
+    """A LoRA workspace, zero-filled as the library requires before its first
+    use (every call returns its counters to zero)."""
+    return torch.zeros(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=device)
+
+
 def gated_lora_apply(x, A, B, is_mask, y, scale=1.0, ws=None, stream=None):
     M, K = x.shape
     r, Nout = A.shape[0], B.shape[0]
     if ws is None:
-        ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
+        ws = lora_workspace(M, r, x.device)
     rc = lib().gated_lora_apply(_p(x), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
                                 _dtype_code(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gated_lora_apply")
@@ -411,7 +417,7 @@ def isd_linear_gated(x, W, A, B, is_mask, scale=1.0, y=None, ws=None, stream=Non
     if y is None:
         y = torch.empty((M, Nout), dtype=ydtype, device=x.device)
     if ws is None:
-        ws = torch.empty(isd_lora_workspace_size(M, r), dtype=torch.uint8, device=x.device)
+        ws = lora_workspace(M, r, x.device)
     rc = lib().isd_linear_gated(_p(x), _p(W), _p(A), _p(B), _p(is_mask), M, K, Nout, r, float(scale), _p(y),
                                 _dtype_code(y), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "isd_linear_gated")

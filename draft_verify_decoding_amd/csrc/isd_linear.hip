@@ -24,6 +24,8 @@
 // in the GEMM's epilogue for isd_linear_gated, in its own kernel for
 // gated_lora_apply, with the same instruction sequence, so the two give the
 // same bits.
+#include <mutex>
+
 #include "isd_common.hpp"
 
 namespace isd {
@@ -130,7 +132,29 @@ struct GemmParams {
   float2* tstats;       // [M][tiles_n] (max, sum exp(l - max)) of the tile's columns
   int tiles_n;
   int yb_vec;           // rows of yb start 16-byte aligned: store them 16 bytes at a time
+  // few rows, gated, one launch: the first nu_blocks workgroups compute U's
+  // split-K partials (A [r][K] into u_out) and count themselves in on
+  // u_ctr[0]; the others wait for that count before their epilogue
+  int nu_blocks;        // 0: U comes from an earlier launch
+  const uint16_t* a;    // [r][K]
+  float* u_out;         // = u, written by this launch
+  int* u_ctr;           // [2] zero between calls: U workgroups done, output workgroups done
 };
+
+// Device-coherent (agent-scope) accesses for values one workgroup of a
+// launch writes and another reads: they reach the point of coherence of the
+// 8 XCDs instead of staying in the writer's L2.
+__device__ __forceinline__ void store_f32_coherent(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_f4_coherent(const float* src) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(src));
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float(static_cast<uint32_t>(a)), __uint_as_float(static_cast<uint32_t>(a >> 32)),
+               __uint_as_float(static_cast<uint32_t>(b)), __uint_as_float(static_cast<uint32_t>(b >> 32))};
+}
+constexpr int kUSpinLimit = 1 << 22;  // polls of the U count before giving up
 
 // One output element, fp32 or rounded to bf16 (nearest even).
 __device__ __forceinline__ void store_y(void* y, bool ybf16, long i, float v) {
@@ -544,7 +568,17 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) float s_u[R16 > 0 ? kARows * kUStride : 4];
 
   const int lane = threadIdx.x, lane32 = lane & 31, hh = lane >> 5;
-  const int n0 = blockIdx.x * 32;
+  // In a gated launch that also computes U (p.nu_blocks > 0), workgroup i <
+  // nu_blocks is U's split-K partial of rank columns 32 (i % ub) .. and split
+  // i / ub, exactly as the ungated partial launch computes it; the others
+  // are the output blocks.
+  constexpr int kRank = 16 * (R16 > 0 ? R16 : 1);
+  constexpr int kUb = (kRank + 31) / 32;  // 32-column blocks of U
+  const bool u_role = R16 > 0 && static_cast<int>(blockIdx.x) < p.nu_blocks;
+  const int yblk = static_cast<int>(blockIdx.x) - p.nu_blocks;
+  const uint16_t* const wmat = u_role ? p.a : p.w;
+  const int nout = u_role ? kRank : p.Nout;
+  const int n0 = u_role ? (static_cast<int>(blockIdx.x) % kUb) * 32 : (R16 > 0 ? yblk : static_cast<int>(blockIdx.x)) * 32;
   // rows m0 .. m0+31 (blockIdx.z > 0 only for the ungated split-K partials;
   // the gated epilogue runs with M <= 32, one row block)
   const int m0 = blockIdx.z * 32;
@@ -560,7 +594,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
     a_src[q] = p.x + static_cast<long>(min(m0 + 8 * q + g_row, p.M - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    b_src[q] = p.w + static_cast<long>(min(n0 + 8 * q + g_row, p.Nout - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
+    b_src[q] = wmat + static_cast<long>(min(n0 + 8 * q + g_row, nout - 1)) * p.K + 8 * ((lane & 7) ^ g_row ^ (q & 1));
   auto load_slab = [&](int k0, int stage) {
     uint16_t* base = stage_ptr(stage);
 #pragma unroll
@@ -590,37 +624,49 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
 
   // split-K (U's partials): split blockIdx.y runs the tiled kernel's share
   // of the slabs, [s nk / splits, (s+1) nk / splits), into its own output
-  const int split = blockIdx.y;
+  const int split = u_role ? static_cast<int>(blockIdx.x) / kUb : static_cast<int>(blockIdx.y);
+  const int splits = u_role ? p.u_splits : p.splits;
   const int nk_all = p.K / kBK;
-  const int kb = split * nk_all / p.splits, nk = (split + 1) * nk_all / p.splits - kb;
+  const int kb = split * nk_all / splits, nk = (split + 1) * nk_all / splits - kb;
 #pragma unroll
   for (int d = 0; d < S - 1; ++d) load_slab((kb + min(d, nk - 1)) * kBK, d);
 
-  // Gated: while the first slabs are in flight, the U rows (split-K
-  // partials summed in split order, as the tiled kernel sums them) go to
-  // LDS and the B fragments and mask bits to registers.
+  // Gated: the U rows (split-K partials summed in split order, as the tiled
+  // kernel sums them) go to LDS, the B fragments and mask bits to registers.
+  // With U from an earlier launch the rows are staged while the first slabs
+  // are in flight; with U computed in this launch, after the K loop, once
+  // every U workgroup has counted itself in.
+  auto stage_u = [&](bool coherent) {
+    if constexpr (R16 > 0) {
+      constexpr int r4 = 4 * R16;
+      const long pstride = static_cast<long>(p.M) * 16 * R16;
+      for (int e = lane; e < p.M * r4; e += 64) {
+        const int row = e / r4, q = e % r4;
+        const float* src = p.u + static_cast<long>(row) * 16 * R16 + 4 * q;
+        f32x4 part[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) {
+          const float* ps = src + (sp < p.u_splits ? sp : 0) * pstride;
+          part[sp] = coherent ? load_f4_coherent(ps) : *reinterpret_cast<const f32x4*>(ps);
+        }
+        f32x4 v = part[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplits; ++sp)
+          if (sp < p.u_splits)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
+        *reinterpret_cast<f32x4*>(&s_u[row * kUStride + 4 * q]) = v;
+      }
+    }
+  };
   int mine = 0;
   BFrag<kR16> bfr;
   if constexpr (R16 > 0) {
-    constexpr int r4 = 4 * R16;
-    const long pstride = static_cast<long>(p.M) * 16 * R16;
-    for (int e = lane; e < p.M * r4; e += 64) {
-      const int row = e / r4, q = e % r4;
-      const float* src = p.u + static_cast<long>(row) * 16 * R16 + 4 * q;
-      f32x4 part[kMaxSplits];
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)
-        part[sp] = *reinterpret_cast<const f32x4*>(src + (sp < p.u_splits ? sp : 0) * pstride);
-      f32x4 v = part[0];
-#pragma unroll
-      for (int sp = 1; sp < kMaxSplits; ++sp)
-        if (sp < p.u_splits)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = v[c] + part[sp][c];
-      *reinterpret_cast<f32x4*>(&s_u[row * kUStride + 4 * q]) = v;
+    if (!u_role) {
+      if (p.nu_blocks == 0) stage_u(false);
+      bfr = b_frag<R16>(p.b, p.Nout, n0, lane32, hh);
+      mine = lane32 < p.M ? p.mask[lane32] != 0 : 0;
     }
-    bfr = b_frag<R16>(p.b, p.Nout, n0, lane32, hh);
-    mine = lane32 < p.M ? p.mask[lane32] != 0 : 0;
   }
 
   // unrolled over S slabs, so every stage index is a constant (as in the
@@ -640,6 +686,58 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
   }
   wait_vm_lgkm0<0>();
 
+  if constexpr (R16 > 0) {
+    if (u_role) {
+      // U's partial of this split: stored device-coherently, completed,
+      // then counted in (no reply needed)
+      const int col = n0 + lane32;
+      float* const dst = p.u_out + static_cast<long>(split) * p.M * kRank;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (row < p.M && col < kRank) store_f32_coherent(dst + static_cast<long>(row) * kRank + col, acc[e]);
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+      if (lane == 0) __hip_atomic_fetch_add(&p.u_ctr[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+  // U computed in this launch: wait (lane 0, bounded) until every U
+  // workgroup has counted itself in, stage the rows, then count this
+  // workgroup in; the last output workgroup returns both counts to zero.
+  // Every workgroup of such a launch fits on the GPU at once (the host
+  // checks), so the U workgroups always run; should the wait still reach
+  // its bound, the MASK rows of this block come out NaN.
+  bool u_ok = true;
+  if constexpr (R16 > 0) {
+    if (p.nu_blocks > 0) {
+      int ok = 1;
+      if (lane == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(&p.u_ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < p.nu_blocks) {
+          if (++spins > kUSpinLimit) {
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      asm volatile("" ::: "memory");
+      u_ok = __shfl(ok, 0) != 0;
+      if (u_ok) stage_u(true);
+      wait_vm_lgkm0<0>();
+      if (lane == 0) {
+        const int ny = static_cast<int>(gridDim.x) - p.nu_blocks;
+        if (__hip_atomic_fetch_add(&p.u_ctr[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ny - 1) {
+          __hip_atomic_fetch_add(&p.u_ctr[0], -p.nu_blocks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&p.u_ctr[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+
   // Epilogue (the tiled kernel's): register e of lane (j, hh) is row
   // 8(e/4) + 4hh + e%4, column j; a MASK row takes acc + scale * delta.
   int live = 0;
@@ -647,7 +745,13 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmParams p) {
   if constexpr (R16 > 0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) live |= __shfl(mine, 8 * (e >> 2) + 4 * hh + (e & 3)) << e;
-    if (__any(live)) dl = lora_delta<R16>(u_frag<R16>(lane32 < p.M ? &s_u[lane32 * kUStride] : nullptr, hh), bfr);
+    if (__any(live)) {
+      if (u_ok)
+        dl = lora_delta<R16>(u_frag<R16>(lane32 < p.M ? &s_u[lane32 * kUStride] : nullptr, hh), bfr);
+      else
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dl[e] = NAN;
+    }
   }
   const int col = n0 + lane32;
   void* const y = p.ybf16 ? static_cast<void*>(static_cast<uint16_t*>(p.y) + static_cast<long>(split) * p.M * p.Nout)
@@ -760,7 +864,8 @@ hipError_t launch_gemm_r(const GemmParams& p, hipStream_t stream) {
   // block and split: each wave keeps all of its split's slabs in flight.
   if (p.M <= 32 || (R16 == 0 && p.splits > 1)) {
     const unsigned mblocks = R16 == 0 ? static_cast<unsigned>((p.M + 31) / 32) : 1u;
-    const dim3 grid(static_cast<unsigned>((p.Nout + 31) / 32), static_cast<unsigned>(p.splits), mblocks);
+    // (with p.nu_blocks > 0 the U workgroups come first in x)
+    const dim3 grid(static_cast<unsigned>(p.nu_blocks + (p.Nout + 31) / 32), static_cast<unsigned>(p.splits), mblocks);
     if (mblocks > 1) hipLaunchKernelGGL((gemm_skinny_kernel<4, R16>), grid, dim3(64), 0, stream, p);
     else if (p.M <= 8) hipLaunchKernelGGL((gemm_skinny_kernel<1, R16>), grid, dim3(64), 0, stream, p);
     else if (p.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<2, R16>), grid, dim3(64), 0, stream, p);
@@ -824,12 +929,17 @@ int u_splits(int K) {
 
 size_t part_bytes(int M, int r) { return (static_cast<size_t>(M) * r * sizeof(float) * kMaxSplits + 255) & ~static_cast<size_t>(255); }
 
-// Split-K partials of U = x A^T at the start of the workspace.
+// LoRA workspace: a counter pair (zero between calls) in its first 256
+// bytes, then U's split-K partials, then U.
+constexpr size_t kLoraCtrlBytes = 256;
+float* lora_parts_of(void* ws) { return reinterpret_cast<float*>(static_cast<char*>(ws) + kLoraCtrlBytes); }
+
+// Split-K partials of U = x A^T into the workspace.
 hipError_t launch_lora_u_partials(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
   GemmParams g{};
   g.x = static_cast<const uint16_t*>(x);
   g.w = static_cast<const uint16_t*>(A);
-  g.y = static_cast<float*>(ws);
+  g.y = lora_parts_of(ws);
   g.M = M;
   g.K = K;
   g.Nout = r;
@@ -841,15 +951,34 @@ hipError_t launch_lora_u_partials(const void* x, const void* A, int M, int K, in
 hipError_t launch_lora_u(const void* x, const void* A, int M, int K, int r, void* ws, hipStream_t stream) {
   hipError_t e = launch_lora_u_partials(x, A, M, K, r, ws, stream);
   if (e != hipSuccess) return e;
-  float* U = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(M, r));
+  float* U = reinterpret_cast<float*>(reinterpret_cast<char*>(lora_parts_of(ws)) + part_bytes(M, r));
   const long n = static_cast<long>(M) * r;
   hipLaunchKernelGGL(lora_u_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const float*>(ws), U, n, u_splits(K));
+                     static_cast<const float*>(lora_parts_of(ws)), U, n, u_splits(K));
   return hipGetLastError();
 }
 
 const float* lora_u_of(void* ws, int M, int r) {
-  return reinterpret_cast<const float*>(static_cast<char*>(ws) + part_bytes(M, r));
+  return reinterpret_cast<const float*>(reinterpret_cast<char*>(lora_parts_of(ws)) + part_bytes(M, r));
+}
+
+// Workgroups of gemm_skinny_kernel<AL, R16> the current GPU holds at once
+// (its occupancy times its CUs), looked up once per device.
+template <int AL, int R16>
+long skinny_capacity() {
+  static std::mutex mu;
+  static long cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && cache[dev] > 0) return cache[dev];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_skinny_kernel<AL, R16>, 64, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const long total = static_cast<long>(per_cu) * isd_device_cus_internal();
+  if (dev >= 0) cache[dev] = total;
+  return total;
 }
 
 hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int M, int Nout, int r, float scale,
@@ -876,6 +1005,25 @@ hipError_t launch_delta(const float* U, const void* B, const uint8_t* mask, int 
     default: hipLaunchKernelGGL(lora_delta_kernel<8>, grid, dim3(256), 0, stream, d); break;
   }
   return hipGetLastError();
+}
+
+// skinny_capacity for the kernel a gated call with M <= 32 rows and rank r
+// launches (the row count picks AL as launch_gemm_r does).
+template <int R16>
+long skinny_capacity_r(int M) {
+  return M <= 8 ? skinny_capacity<1, R16>() : (M <= 16 ? skinny_capacity<2, R16>() : skinny_capacity<4, R16>());
+}
+long skinny_capacity_of(int M, int r) {
+  switch (r / 16) {
+    case 1: return skinny_capacity_r<1>(M);
+    case 2: return skinny_capacity_r<2>(M);
+    case 3: return skinny_capacity_r<3>(M);
+    case 4: return skinny_capacity_r<4>(M);
+    case 5: return skinny_capacity_r<5>(M);
+    case 6: return skinny_capacity_r<6>(M);
+    case 7: return skinny_capacity_r<7>(M);
+    default: return skinny_capacity_r<8>(M);
+  }
 }
 
 int check_gemm_args(const void* x, const void* W, int M, int K, int Nout, const void* y, int ydtype) {
@@ -920,7 +1068,7 @@ int isd_linear(const void* x, const void* W, int M, int K, int Nout, void* y, in
 
 size_t isd_lora_workspace_size(int M, int r) {
   if (M < 0 || r < 0) return 0;
-  return part_bytes(M, r) + static_cast<size_t>(M) * r * sizeof(float);
+  return kLoraCtrlBytes + part_bytes(M, r) + static_cast<size_t>(M) * r * sizeof(float);
 }
 
 int gated_lora_apply(const void* x, const void* A, const void* B, const uint8_t* is_mask, int M, int K, int Nout,
@@ -947,15 +1095,25 @@ int isd_linear_gated(const void* x, const void* W, const void* A, const void* B,
   rc = isd_check_device_internal();
   if (rc) return rc;
   // U's split-K partials; the GEMM sums them (in split order, as the
-  // reduction kernel of gated_lora_apply does) when it stages its U rows
-  if (launch_lora_u_partials(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
+  // reduction kernel of gated_lora_apply does) when it stages its U rows.
+  // Few rows: U's workgroups join the GEMM's launch when all of its
+  // workgroups fit on the GPU at once; otherwise U has a launch of its own.
+  const int nu = (r + 31) / 32 * u_splits(K);
+  const bool one_launch = M <= 32 && nu + (static_cast<long>(Nout) + 31) / 32 <= skinny_capacity_of(M, r);
+  if (!one_launch && launch_lora_u_partials(x, A, M, K, r, ws, stream) != hipSuccess) return ISD_E_LAUNCH;
   GemmParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(W);
   p.y = y;
   p.ybf16 = ydtype == ISD_BF16;
-  p.u = static_cast<const float*>(ws);
+  p.u = lora_parts_of(ws);
   p.u_splits = u_splits(K);
+  if (one_launch) {
+    p.nu_blocks = nu;
+    p.a = static_cast<const uint16_t*>(A);
+    p.u_out = lora_parts_of(ws);
+    p.u_ctr = static_cast<int*>(ws);
+  }
   p.b = static_cast<const uint16_t*>(B);
   p.mask = is_mask;
   p.scale = scale;

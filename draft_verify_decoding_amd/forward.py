@@ -14,7 +14,7 @@ Model Zoo"); the pages do not describe it.
 import torch
 
 from . import (KVCache, accept_workspace, isd_attention_workspace_size, isd_lm_head_workspace_size,
-               isd_lora_workspace_size, prepare_attention, prepare_cast_bf16, prepare_linear, prepare_linear_gated,
+               isd_lora_workspace_size, lora_workspace, prepare_attention, prepare_cast_bf16, prepare_linear, prepare_linear_gated,
                prepare_lm_head, prepare_rmsnorm, prepare_swiglu)
 
 
@@ -75,7 +75,7 @@ class Forward:
         r_max = max([0] + ranks)
         split = layers[0].qkv_adapters is not None
         widths = [Hq * D, Hkv * D, Hkv * D]
-        self.lora_ws = e(max(isd_lora_workspace_size(M, max(r_max, 16)), 256) // 4)
+        self.lora_ws = lora_workspace(M, max(r_max, 16), dev)  # zero-filled
         need = isd_attention_workspace_size(kvs[0], C, R, Hq, max_len, slices)
         self.att_ws = e(max(need, 256) // 4 + 1)
         self.lm_ws = e(isd_lm_head_workspace_size(M, V) // 4 + 1)

@@ -339,12 +339,16 @@ int isd_block_assemble(const isd_seq_state* st, const int32_t* emit,
  * is_mask[m] != 0; A [r][K] and B [Nout][r] bf16; other rows are never
  * written. U = x A^T (fp32, a split-K GEMM whose split count depends on K
  * only) is built in the workspace, which must hold
- * isd_lora_workspace_size(M, r) bytes (16-byte aligned, owned by the caller,
- * contents on entry ignored).
+ * isd_lora_workspace_size(M, r) bytes (16-byte aligned, owned by the
+ * caller). Its first 256 bytes are counters: zero-fill the workspace once
+ * before its first use; every call returns them to zero (at any M, r), the
+ * rest is scratch. Calls that share a workspace must not overlap in time.
  * isd_linear_gated: y = isd_linear(x, W) then gated_lora_apply, with the
  * delta added in the base GEMM's epilogue; its clean rows equal isd_linear's
  * bit for bit and, with fp32 y, its MASK rows equal those of the two
- * separate calls. With bf16 y, gated_lora_apply reads y, adds the delta in
+ * separate calls. With M <= 32 and every workgroup of the call resident on
+ * the GPU at once, U is computed by extra workgroups of the GEMM's own
+ * launch (one launch instead of two); the bits are the same either way. With bf16 y, gated_lora_apply reads y, adds the delta in
  * fp32 and rounds again, so the separate calls' MASK rows carry a second
  * rounding that the fused call does not.
  * x, W, A, B must be 16-byte aligned, all row-major and contiguous.

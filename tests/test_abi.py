@@ -155,7 +155,8 @@ def test_linear_rejects_bad_arguments_on_host(lib):
     assert lib.isd_linear(16, 16, 4, 64, 8, 17, BF16, None) == -1  # bf16 output not 2-byte aligned
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 24, 1.0, 16, F32, 16, 1 << 20, None) == -2  # rank 24
     assert lib.gated_lora_apply(16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, F32, 16, 8, None) == -3  # ws too small
-    assert lib.isd_lora_workspace_size(512, 32) == 512 * 32 * 4 * 9  # 8 split-K partials of U, then U
+    # a 256-byte counter pair, 8 split-K partials of U, then U
+    assert lib.isd_lora_workspace_size(512, 32) == 256 + 512 * 32 * 4 * 9
     assert lib.gated_lora_apply(16, 16, 24, 16, 4, 64, 8, 32, 1.0, 16, F32, 16, 512, None) == -1  # B misaligned
     assert lib.isd_linear_gated(16, 16, 16, 16, 16, 4, 64, 8, 32, 1.0, 16, 0, 16, 1 << 20, None) == -2  # type
 
