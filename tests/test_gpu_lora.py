@@ -260,3 +260,30 @@ def test_bf16_output_is_the_rounded_fp32_output(M):
     want = ref.gated_lora(x.double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(), mask, 1.0)
     got = fused16.float().cpu().double().numpy()
     assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-4 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("M,r", [(8, 96), (32, 32)])
+def test_few_rows_one_launch_and_two_launch_paths_agree(M, r):
+    """With up to 32 rows U's split-K workgroups join the GEMM's launch when
+    the whole grid is resident on the GPU at once; a wider output (20,480
+    columns: 640 column blocks plus U's) does not fit, and U then has a launch
+    of its own. A column block's outputs do not depend on the width, so the
+    narrow call (one launch) equals the first columns of the wide call (two
+    launches) bit for bit, call after call on one workspace, whose counter
+    pair is back at zero after every call; the narrow call matches the
+    oracle."""
+    K, Nw, Nn = 4096, 20480, 4096
+    x, W, A, B, mask = case(12, M, K, Nw, r)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    ws = dvd.lora_workspace(M, r)
+    wide = dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=0.5, ws=ws)
+    Wn, Bn = Wd[:Nn].contiguous(), Bd[:Nn].contiguous()
+    narrow = [dvd.isd_linear_gated(xd, Wn, Ad, Bn, md, scale=0.5, ws=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert int(ws[:256].count_nonzero()) == 0
+    for y in narrow:
+        assert torch.equal(y.view(torch.int32), wide[:, :Nn].view(torch.int32))
+    want = ref.gated_lora(x.double().numpy(), W[:Nn].double().numpy(), A.double().numpy(), B[:Nn].double().numpy(),
+                          mask, 0.5)
+    assert rel_err(narrow[0].cpu().double().numpy(), want) < 2e-3
