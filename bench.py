@@ -546,6 +546,42 @@ def cpu_baseline(cfg, fwd_seqs=8, accept_seqs=48, accept_steps=14, layers_timed=
                 host_cores_affinity=len(os.sched_getaffinity(0)), host_cores_os=os.cpu_count())
 
 
+def read_probe():
+    """HBM rates that plain vendor kernels reach on this GPU: torch's sum of
+    a 4 GiB bf16 tensor (fp32 accumulation: reads 4 GiB, writes 4 bytes), the
+    vendor BLAS matrix-vector product over the same 4 GiB as a 65536 x 32768
+    matrix, and a 1 GiB device copy (reads and writes 1 GiB), each timed on
+    HIP events over 10 calls after 3 warmup calls, on the stream the kernels
+    run on."""
+    torch.cuda.set_device(0)
+    n = 1 << 31
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    out = {}
+
+    def timed(fn, nbytes, name):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 100.0  # ms over 10 calls -> us per call
+        out[name] = {"us_per_call": round(us, 2), "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1)}
+
+    timed(lambda: torch.sum(x, dtype=torch.float32), 2 * n, "sum_bf16_4GiB")
+    # the vendor BLAS matrix-vector product: a 4 GiB bf16 matrix read once
+    mat = x.view(1 << 16, 1 << 15)
+    vec = torch.ones(1 << 15, dtype=torch.bfloat16, device="cuda")
+    timed(lambda: torch.mv(mat, vec), 2 * n, "gemv_bf16_4GiB")
+    src = x[: 1 << 29]
+    dst = torch.empty_like(src)
+    timed(lambda: dst.copy_(src), 2 * 2 * (1 << 29), "copy_1GiB")
+    print(json.dumps({"read_probe": out, "peak_gbps": HBM_PEAK_GBPS}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -582,6 +618,9 @@ def main():
     ap.add_argument("--forward-steps", type=int, default=6, help="timed steps of each whole-forward configuration")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for counter scaling)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only time vendor streaming kernels (a 4 GiB bf16 sum and matrix-vector product, a 1 GiB copy) on HIP events: "
+                         "the read rate the chip gives a plain stream, beside the attention's")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print per-kernel means of a rocprofv3 --pmc CSV output directory and exit")
     ap.add_argument("--algo-out", metavar="FILE",
@@ -602,6 +641,9 @@ def main():
         args.slices = {"8b": -64, "8b1": -4, "32b": -66}[args.workload]
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
+        return
+    if args.read_probe:
+        read_probe()
         return
     if args.copy_probe:
         torch.cuda.set_device(0)

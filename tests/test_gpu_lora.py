@@ -287,3 +287,25 @@ def test_few_rows_one_launch_and_two_launch_paths_agree(M, r):
     want = ref.gated_lora(x.double().numpy(), W[:Nn].double().numpy(), A.double().numpy(), B[:Nn].double().numpy(),
                           mask, 0.5)
     assert rel_err(narrow[0].cpu().double().numpy(), want) < 2e-3
+
+
+@pytest.mark.parametrize("M,K,Nout,r", [(512, 4096, 6144, 96), (512, 4096, 4096, 32), (200, 4096, 4096, 128),
+                                        (128, 5120, 10240, 96), (72, 4096, 1024, 16)])
+def test_tiled_fused_call_matches_separate_calls(M, K, Nout, r):
+    """Above 32 rows (tiled kernels, every tile shape the picker takes here,
+    ragged row counts, ranks 16 to 128): the fused call equals isd_linear
+    followed by gated_lora_apply bit for bit on every row, call after call on
+    one workspace, whose counter bytes stay zero; it matches the oracle."""
+    x, W, A, B, mask = case(13, M, K, Nout, r)
+    xd, Wd, Ad, Bd = dev(x, W, A, B)
+    md = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    ws = dvd.lora_workspace(M, r)
+    sep = dvd.isd_linear(xd, Wd)
+    dvd.gated_lora_apply(xd, Ad, Bd, md, sep, scale=0.75, ws=ws)
+    fused = [dvd.isd_linear_gated(xd, Wd, Ad, Bd, md, scale=0.75, ws=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert int(ws[:256].count_nonzero()) == 0
+    for y in fused:
+        assert torch.equal(y.view(torch.int32), sep.view(torch.int32))
+    want = ref.gated_lora(x.double().numpy(), W.double().numpy(), A.double().numpy(), B.double().numpy(), mask, 0.75)
+    assert rel_err(fused[0].cpu().double().numpy(), want) < 2e-3
