@@ -157,17 +157,17 @@ def test_bad_page_id_sets_device_flag():
     assert err.item() & dvd.DEV_PAGE_OOB
 
 
-@pytest.mark.parametrize("slices", [0, dvd.attn_invariant(4), dvd.attn_invariant(1)])
+@pytest.mark.parametrize("slices", [0, dvd.attn_invariant(8), dvd.attn_invariant(4), dvd.attn_invariant(1)])
 def test_8b_single_sequence_context_4096(slices):
     """C=1, N=4, 32/8 heads, D=128, 4096 cached tokens: every output checked,
-    in the stream-K split and in the batch-invariant split with chunks of 4
-    tiles (the single-sequence step's launch) and of 1 tile."""
+    in the stream-K split and in the batch-invariant split with chunks of 8
+    tiles (the single-sequence step's launch), 4 and 1 tile."""
     case = workload.AttentionCase(2, C=1, rows=8, Hq=32, Hkv=8, D=128, ctx=4096)
     got, want = run(case, slices=slices)
     assert slab_errors(got, want).max() < 2e-3
 
 
-@pytest.mark.parametrize("t", [4, 1])
+@pytest.mark.parametrize("t", [8, 4, 1])
 def test_single_sequence_equals_its_rows_in_a_wide_batch(t):
     """A single sequence runs on a grid of its own shape (few chunks: one KV
     head per workgroup) and a 64-sequence batch on another (eight heads per
@@ -407,17 +407,21 @@ def test_kv_write_layers_equals_per_layer_calls():
     assert err.item() == 0
 
 
-@pytest.mark.parametrize("shape", ["8b", "32b"])
+@pytest.mark.parametrize("shape", ["8b", "8b1", "32b"])
 def test_timed_launch_configuration_against_the_oracle(shape):
     """The call the step benchmark times, at its full shapes: the block's K/V
     read from its rows (pages hold only the cached context), the
     batch-invariant split with 64-tile chunks (8B: C=64, 32/8 heads, ragged
-    1K-8K contexts) or 66-tile chunks (32B: C=16, 64/8 heads, 16,384
-    cached tokens). The whole batch runs and every sequence is checked
-    against the oracle in full."""
+    1K-8K contexts), 8-tile chunks (8B, one sequence of 4,096 cached tokens)
+    or 66-tile chunks (32B: C=16, 64/8 heads, 16,384 cached tokens). The
+    whole batch runs and every sequence is checked against the oracle in
+    full."""
     if shape == "8b":
         case = workload.AttentionCase(81, C=64, rows=8, Hq=32, Hkv=8, D=128, ctx=("uniform", 1024, 8192))
         t = 64
+    elif shape == "8b1":
+        case = workload.AttentionCase(83, C=1, rows=8, Hq=32, Hkv=8, D=128, ctx=4096)
+        t = 8
     else:
         case = workload.AttentionCase(82, C=16, rows=8, Hq=64, Hkv=8, D=128, ctx=16384)
         t = 66
